@@ -1,0 +1,199 @@
+"""Twilight hierarchical top-p sparse decode attention for MI355X (gfx950).
+
+Thin Python binding over ``libtwilight.so``: argument marshalling only. Every step of the
+path runs in the HIP kernels behind the C ABI declared in ``include/twilight.h``; the
+functions below take torch tensors that live on the GPU, pass their device pointers and the
+current HIP stream, and raise ``TwilightError`` on a negative status. There is no CPU
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtwilight.so")
+PAGE_SIZE = 16
+
+TWL_OK = 0
+TWL_ERR_INVALID_ARG = -1
+TWL_ERR_UNSUPPORTED = -2
+TWL_ERR_WORKSPACE = -3
+TWL_ERR_LAUNCH = -4
+
+EXPORTED = ("twilight_quantize_keys", "quest_page_bounds", "quest_select_pages",
+            "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode",
+            "twilight_workspace_size", "twilight_status_string")
+
+
+class TwilightError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    """Mirror of twl_layout_t."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("num_phys_pages", ctypes.c_int32), ("page_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtwilight.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python adaptive_top_sparse_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        LP = ctypes.POINTER(Layout)
+        L.twilight_quantize_keys.argtypes = [LP, P, P, P, P, P]
+        L.quest_page_bounds.argtypes = [LP, P, P, P, P]
+        L.quest_select_pages.argtypes = [LP, P, P, I32, P, P, P, SZ, P]
+        L.twilight_estimate_weights.argtypes = [LP, P, P, P, P, P, I32, F, P, P, SZ, P]
+        L.twilight_topp_select.argtypes = [LP, P, P, P, I32, F, P, P, P, P, SZ, P]
+        L.twilight_sparse_decode.argtypes = [LP, P, P, P, P, P, I32, F, P, P, SZ, P]
+        for name in EXPORTED[:6]:
+            getattr(L, name).restype = ctypes.c_int
+        L.twilight_workspace_size.argtypes = [LP, I32]
+        L.twilight_workspace_size.restype = ctypes.c_size_t
+        L.twilight_status_string.argtypes = [ctypes.c_int]
+        L.twilight_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().twilight_status_string(int(status)).decode()
+
+
+# ---- marshalling helpers -----------------------------------------------------------------
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous GPU tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != TWL_OK:
+        raise TwilightError(fn, status)
+
+
+def make_layout(page_table, seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                num_phys_pages: int) -> Layout:
+    """twl_layout_t for int32 GPU tensors page_table [B, max_pages] and seq_lens [B].
+
+    The tensors must outlive every call made with the layout."""
+    import torch
+    B, max_pages = page_table.shape
+    return Layout(batch=B, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                  head_dim=head_dim, page_size=PAGE_SIZE, max_pages_per_seq=max_pages,
+                  num_phys_pages=num_phys_pages,
+                  page_table=_ptr(page_table, torch.int32, "page_table"),
+                  seq_lens=_ptr(seq_lens, torch.int32, "seq_lens"))
+
+
+# ---- the C ABI, one function each -------------------------------------------------------
+
+def twilight_workspace_size(layout: Layout, cand_stride_pages: int) -> int:
+    return int(lib().twilight_workspace_size(ctypes.byref(layout), int(cand_stride_pages)))
+
+
+def twilight_quantize_keys(layout: Layout, k_cache, k_codes, k_meta, token_begin=None,
+                           stream=None) -> None:
+    import torch
+    st = lib().twilight_quantize_keys(
+        ctypes.byref(layout), _ptr(k_cache, torch.float16, "k_cache"),
+        _ptr(token_begin, torch.int32, "token_begin"), _ptr(k_codes, torch.uint8, "k_codes"),
+        _ptr(k_meta, torch.float16, "k_meta"), _stream(stream))
+    _check("twilight_quantize_keys", st)
+
+
+def quest_page_bounds(layout: Layout, k_cache, page_minmax, token_begin=None,
+                      stream=None) -> None:
+    import torch
+    st = lib().quest_page_bounds(
+        ctypes.byref(layout), _ptr(k_cache, torch.float16, "k_cache"),
+        _ptr(token_begin, torch.int32, "token_begin"),
+        _ptr(page_minmax, torch.float16, "page_minmax"), _stream(stream))
+    _check("quest_page_bounds", st)
+
+
+def quest_select_pages(layout: Layout, q, page_minmax, budget_pages: int, sel_pages, sel_count,
+                       workspace, stream=None) -> None:
+    import torch
+    st = lib().quest_select_pages(
+        ctypes.byref(layout), _ptr(q, torch.float16, "q"),
+        _ptr(page_minmax, torch.float16, "page_minmax"), int(budget_pages),
+        _ptr(sel_pages, torch.int32, "sel_pages"), _ptr(sel_count, torch.int32, "sel_count"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("quest_select_pages", st)
+
+
+def twilight_estimate_weights(layout: Layout, q, k_codes, k_meta, cand_pages, cand_count,
+                              cand_stride_pages: int, sm_scale: float, weights, workspace,
+                              stream=None) -> None:
+    import torch
+    st = lib().twilight_estimate_weights(
+        ctypes.byref(layout), _ptr(q, torch.float16, "q"), _ptr(k_codes, torch.uint8, "k_codes"),
+        _ptr(k_meta, torch.float16, "k_meta"), _ptr(cand_pages, torch.int32, "cand_pages"),
+        _ptr(cand_count, torch.int32, "cand_count"), int(cand_stride_pages), float(sm_scale),
+        _ptr(weights, torch.float32, "weights"), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("twilight_estimate_weights", st)
+
+
+def twilight_topp_select(layout: Layout, weights, cand_pages, cand_count,
+                         cand_stride_pages: int, p: float, kept, kept_count, tau, workspace,
+                         stream=None) -> None:
+    import torch
+    st = lib().twilight_topp_select(
+        ctypes.byref(layout), _ptr(weights, torch.float32, "weights"),
+        _ptr(cand_pages, torch.int32, "cand_pages"), _ptr(cand_count, torch.int32, "cand_count"),
+        int(cand_stride_pages), float(p), _ptr(kept, torch.int32, "kept"),
+        _ptr(kept_count, torch.int32, "kept_count"), _ptr(tau, torch.float32, "tau"),
+        _ptr(workspace, None, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("twilight_topp_select", st)
+
+
+def twilight_sparse_decode(layout: Layout, q, k_cache, v_cache, kept, kept_count,
+                           kept_stride: int, sm_scale: float, out, workspace,
+                           stream=None) -> None:
+    import torch
+    st = lib().twilight_sparse_decode(
+        ctypes.byref(layout), _ptr(q, torch.float16, "q"), _ptr(k_cache, torch.float16, "k_cache"),
+        _ptr(v_cache, torch.float16, "v_cache"), _ptr(kept, torch.int32, "kept"),
+        _ptr(kept_count, torch.int32, "kept_count"), int(kept_stride), float(sm_scale),
+        _ptr(out, torch.float16, "out"), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("twilight_sparse_decode", st)

@@ -1,0 +1,58 @@
+// Host-side launchers of the Twilight kernels (internal to libtwilight.so). Arguments are
+// validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace twl {
+
+// Tokens per KV-cache page.
+constexpr int kPage = 16;
+
+struct Layout {
+  int B, Hq, Hkv, d, max_pages, num_phys;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int G() const { return Hq / Hkv; }
+};
+
+// Rows of candidate slots are processed in chunks of this many slots by the estimate.
+constexpr int kEstChunk = 256;
+
+// Kept tokens per decode work-group for a given kept stride and unit count.
+int decode_chunk_tokens(const Layout& L, int kept_stride);
+
+size_t quest_workspace_bytes(const Layout& L);
+size_t estimate_workspace_bytes(const Layout& L, int cand_stride_pages);
+size_t decode_workspace_bytes(const Layout& L, int kept_stride);
+size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages);
+
+hipError_t launch_quantize_keys(const Layout& L, const void* k_cache, const int32_t* token_begin,
+                                uint8_t* codes, void* meta, hipStream_t s);
+hipError_t launch_page_bounds(const Layout& L, const void* k_cache, const int32_t* token_begin,
+                              void* minmax, hipStream_t s);
+hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
+                               int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s);
+hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes, const void* meta,
+                           const int32_t* cand_pages, const int32_t* cand_count,
+                           int cand_stride_pages, float sm_scale, float* weights, void* ws,
+                           hipStream_t s);
+hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* cand_pages,
+                       const int32_t* cand_count, int cand_stride_pages, float p,
+                       int32_t* kept, int32_t* kept_count, float* tau, void* ws,
+                       hipStream_t s);
+hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* kept,
+                                const int32_t* kept_count, int kept_stride, float sm_scale,
+                                void* out, void* ws, hipStream_t s);
+
+// Largest slot count per unit the top-p kernel holds on chip.
+constexpr int kToppMaxSlots = 65536;
+// Largest page count per sequence the Quest selector holds on chip.
+constexpr int kQuestMaxPages = 32768;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace twl

@@ -1,0 +1,151 @@
+"""Device buffers and the decode step of the Twilight hot path, driven through the C ABI.
+
+A step is the select-then-prune pipeline of the Twilight pages (atlas.scime.ai summary,
+"Approach"): Quest page selection (skipped when every token is a candidate), the int4
+weight estimate, top-p thresholding with compaction, and sparse decode over the kept
+tokens. torch only allocates device memory here; every stage runs in libtwilight.so.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import (PAGE_SIZE, make_layout, quest_page_bounds, quest_select_pages,
+               twilight_estimate_weights, twilight_quantize_keys, twilight_sparse_decode,
+               twilight_topp_select, twilight_workspace_size)
+
+
+def default_sm_scale(d: int) -> float:
+    """The attention scale 1/sqrt(d), rounded to fp32 as the ABI receives it."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+@dataclasses.dataclass
+class DeviceCache:
+    """One layer's paged caches and tables on the GPU."""
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    budget: Optional[int]
+    num_phys: int
+    page_table: torch.Tensor
+    seq_lens: torch.Tensor
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    k_codes: torch.Tensor
+    k_meta: torch.Tensor
+    page_minmax: Optional[torch.Tensor]
+
+    def layout(self):
+        return make_layout(self.page_table, self.seq_lens, self.Hq, self.Hkv, self.d,
+                           self.num_phys)
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    @property
+    def cand_stride_pages(self) -> int:
+        return self.budget if self.budget is not None else self.max_pages
+
+    def build_caches(self, stream=None) -> None:
+        """Quantize every key and compute every page's bounds (prefill-time maintenance)."""
+        lay = self.layout()
+        twilight_quantize_keys(lay, self.k_cache, self.k_codes, self.k_meta, stream=stream)
+        if self.page_minmax is not None:
+            quest_page_bounds(lay, self.k_cache, self.page_minmax, stream=stream)
+
+    def clone(self) -> "DeviceCache":
+        """A replica at distinct addresses (for cache-defeating layer rotation)."""
+        rep = {}
+        for f in dataclasses.fields(self):
+            v = getattr(self, f.name)
+            rep[f.name] = v.clone() if isinstance(v, torch.Tensor) else v
+        return DeviceCache(**rep)
+
+
+def upload(w, device="cuda", with_bounds: Optional[bool] = None) -> DeviceCache:
+    """Copy a workloads.Workload to the GPU (caches in the paged layout) and allocate the
+    int4 key cache and the page bounds it needs."""
+    s = w.spec
+    dev = torch.device(device)
+    budget = w.budget
+    if with_bounds is None:
+        with_bounds = budget is not None
+    k_paged = torch.from_numpy(w.paged("k")).to(dev)
+    v_paged = torch.from_numpy(w.paged("v")).to(dev)
+    P = w.num_phys_pages
+    return DeviceCache(
+        B=s.B, Hq=s.Hq, Hkv=s.Hkv, d=s.d, budget=budget, num_phys=P,
+        page_table=torch.from_numpy(w.page_table).to(dev),
+        seq_lens=torch.from_numpy(w.seq_lens).to(dev),
+        q=torch.from_numpy(w.q).to(dev),
+        k_cache=k_paged, v_cache=v_paged,
+        k_codes=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 2), dtype=torch.uint8, device=dev),
+        k_meta=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 32, 2), dtype=torch.float16, device=dev),
+        page_minmax=(torch.zeros((P, s.Hkv, 2, s.d), dtype=torch.float16, device=dev)
+                     if with_bounds else None))
+
+
+@dataclasses.dataclass
+class StepBuffers:
+    """Outputs of every stage of one step, plus the shared workspace."""
+    sel_pages: Optional[torch.Tensor]
+    sel_count: Optional[torch.Tensor]
+    weights: torch.Tensor
+    kept: torch.Tensor
+    kept_count: torch.Tensor
+    tau: torch.Tensor
+    out: torch.Tensor
+    workspace: torch.Tensor
+
+
+def alloc_step(c: DeviceCache) -> StepBuffers:
+    dev = c.q.device
+    stride = c.cand_stride_pages
+    n_slots = stride * PAGE_SIZE
+    ws_bytes = twilight_workspace_size(c.layout(), stride)
+    if ws_bytes == 0:
+        raise ValueError("layout rejected by twilight_workspace_size")
+    return StepBuffers(
+        sel_pages=(torch.full((c.B, c.Hkv, stride), -1, dtype=torch.int32, device=dev)
+                   if c.budget is not None else None),
+        sel_count=(torch.zeros((c.B, c.Hkv), dtype=torch.int32, device=dev)
+                   if c.budget is not None else None),
+        weights=torch.zeros((c.B, c.Hq, n_slots), dtype=torch.float32, device=dev),
+        kept=torch.full((c.B, c.Hkv, n_slots), -1, dtype=torch.int32, device=dev),
+        kept_count=torch.zeros((c.B, c.Hkv), dtype=torch.int32, device=dev),
+        tau=torch.zeros((c.B, c.Hkv), dtype=torch.float32, device=dev),
+        out=torch.zeros((c.B, c.Hq, c.d), dtype=torch.float16, device=dev),
+        # zero-filled once; the library needs no particular contents
+        workspace=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev))
+
+
+def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[float] = None,
+             stream=None, stages=("select", "estimate", "topp", "decode")) -> None:
+    """One decode step of the hot path on `stream` (no host synchronization)."""
+    if sm_scale is None:
+        sm_scale = default_sm_scale(c.d)
+    lay = c.layout()
+    stride = c.cand_stride_pages
+    if c.budget is not None and "select" in stages:
+        quest_select_pages(lay, c.q, c.page_minmax, c.budget, buf.sel_pages, buf.sel_count,
+                           buf.workspace, stream=stream)
+    cand_pages = buf.sel_pages if c.budget is not None else None
+    cand_count = buf.sel_count if c.budget is not None else None
+    if "estimate" in stages:
+        twilight_estimate_weights(lay, c.q, c.k_codes, c.k_meta, cand_pages, cand_count, stride,
+                                  sm_scale, buf.weights, buf.workspace, stream=stream)
+    if "topp" in stages:
+        twilight_topp_select(lay, buf.weights, cand_pages, cand_count, stride, p, buf.kept,
+                             buf.kept_count, buf.tau, buf.workspace, stream=stream)
+    if "decode" in stages:
+        twilight_sparse_decode(lay, c.q, c.k_cache, c.v_cache, buf.kept, buf.kept_count,
+                               stride * PAGE_SIZE, sm_scale, buf.out, buf.workspace,
+                               stream=stream)

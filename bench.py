@@ -1,0 +1,256 @@
+"""Benchmark of one Twilight sparse decode step on one MI355X.
+
+A step is the whole hot path for one decode layer: Quest page selection, the int4 weight
+estimate, top-p with compaction, and sparse decode over the kept tokens (the
+select-then-prune pipeline of the Twilight pages, atlas.scime.ai summary "Approach").
+Inputs are synthetic and already resident in HBM. To keep the 256 MB Infinity Cache and
+the L2 from serving a step out of cache, consecutive steps rotate over independent layer
+replicas (distinct buffers), as consecutive layers of a real decode do.
+
+Prints ONE JSON line. `value` is candidate tokens per second: sum over (sequence, KV head)
+of the candidate count, divided by the step time (hipGraph launch).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn µs/decode step & candidate tokens/s at 1 GPU; % of HBM peak"
+HBM_PEAK = 8.0e12            # MI355X HBM3E, bytes/s
+PAGE = 16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def stage_bytes(c, buf, d):
+    """Algorithmic bytes per stage (each byte the method must move counted once)."""
+    import torch
+    B, Hq, Hkv = c.B, c.Hq, c.Hkv
+    G = Hq // Hkv
+    seq = c.seq_lens.cpu().numpy().astype(np.int64)
+    pages = -(-seq // PAGE)
+    stride = c.cand_stride_pages
+    if c.budget is not None:
+        sel_count = buf.sel_count.cpu().numpy().astype(np.int64)          # [B, Hkv]
+        sel = buf.sel_pages.cpu().numpy().astype(np.int64)
+        cand = np.zeros((B, Hkv), np.int64)
+        for b in range(B):
+            for g in range(Hkv):
+                pg = sel[b, g, :sel_count[b, g]]
+                cand[b, g] = int(np.minimum(seq[b] - pg * PAGE, PAGE).clip(0).sum())
+    else:
+        sel_count = None
+        cand = np.repeat(seq[:, None], Hkv, axis=1)
+    kept = buf.kept_count.cpu().numpy().astype(np.int64)
+    qo = B * Hq * d * 2
+    out = {}
+    if c.budget is not None:
+        out["quest_select_pages"] = int(pages.sum() * Hkv * (2 * d * 2) + qo + sel_count.sum() * 4)
+    int4_row = d // 2 + (d // 32) * 4
+    out["twilight_estimate_weights"] = int(cand.sum() * int4_row + cand.sum() * G * 4 + qo)
+    out["twilight_topp_select"] = int(cand.sum() * G * 4 + kept.sum() * 4)
+    out["twilight_sparse_decode"] = int(kept.sum() * (2 * d * 2 + 4) + 2 * qo)
+    return out, int(cand.sum()), int(kept.sum())
+
+
+def cpu_baseline(w, p, seconds):
+    """The fp64 oracle (stages select, estimate, top-p, attention; the cache is quantized
+    beforehand, as on the GPU) on whole decode steps of the same workload, single thread,
+    repeated until `seconds` have passed."""
+    import oracle
+    s = w.spec
+    G = s.G
+    sm = float(np.float32(1.0 / math.sqrt(s.d)))
+    # a bounded sample: the first two (sequence, KV head) units of the step
+    units = [(b, g) for b in range(s.B) for g in range(s.Hkv)][:2]
+    prep = {}
+    for b, g in units:
+        k = w.k[b][g]
+        codes, scale, zero = oracle.quantize_keys(k)
+        lo, hi = oracle.page_bounds(k) if w.budget is not None else (None, None)
+        prep[(b, g)] = (codes, scale, zero, lo, hi)
+    cand_total = 0
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for b, g in units:
+            codes, scale, zero, lo, hi = prep[(b, g)]
+            qg = w.q[b, g * G:(g + 1) * G]
+            n = int(w.seq_lens[b])
+            if w.budget is not None:
+                sel = oracle.quest_select(qg, lo, hi, w.budget)
+                n_slots = w.budget * PAGE
+                tok = np.repeat(sel.astype(np.int64), PAGE) * PAGE + np.tile(np.arange(PAGE), len(sel))
+                valid = np.zeros(n_slots, bool)
+                valid[:tok.size] = tok < n
+            else:
+                sel = None
+                n_slots = -(-n // PAGE) * PAGE
+                valid = np.arange(n_slots) < n
+            wts = oracle.estimate_weights(qg, codes, scale, zero, n, sel, n_slots, sm)
+            kept, _ = oracle.topp_select(wts, valid, p, sel)
+            oracle.sparse_attention(qg, w.k[b][g], w.v[b][g], kept, sm)
+            cand_total += int(valid.sum())
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": cand_total / el, "unit": "candidate tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} passes over {len(units)} (sequence, KV head) units of the "
+                      f"same workload (select, estimate, top-p, attention), single-threaded "
+                      f"fp64 oracle, {el:.1f} s; cache quantization excluded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the hot path "
+              "is a single-GPU kernel library and this build has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import adaptive_top_sparse_amd as twl
+    from adaptive_top_sparse_amd import pipeline, workloads
+
+    torch.cuda.set_device(0)
+    spec = workloads.SPECS[args.config]
+    p = args.p if args.p is not None else spec.ps[len(spec.ps) // 2]
+    t_gen = time.perf_counter()
+    w = workloads.make_workload(args.config)
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] generated config {args.config} ({spec.name}) in {t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+    base = pipeline.upload(w)
+    stream = torch.cuda.Stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # cache maintenance (prefill-time quantization and page bounds), timed once
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        base.build_caches(stream=stream)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = ev0.elapsed_time(ev1)
+    reps = [base] + [base.clone() for _ in range(args.replicas - 1)]
+    bufs = [pipeline.alloc_step(r) for r in reps]
+    torch.cuda.synchronize()
+    print(f"[bench] {len(reps)} layer replicas resident; warming up", file=sys.stderr, flush=True)
+
+    def step(i):
+        pipeline.run_step(reps[i % len(reps)], bufs[i % len(reps)], p, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    # plain launches, with events around every ABI call to time the stages
+    names = (["quest_select_pages"] if base.budget is not None else []) + [
+        "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode"]
+    stage_map = {"quest_select_pages": "select", "twilight_estimate_weights": "estimate",
+                 "twilight_topp_select": "topp", "twilight_sparse_decode": "decode"}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_plain0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            r = i % len(reps)
+            evs[i][0].record(stream)
+            for j, nm in enumerate(names):
+                pipeline.run_step(reps[r], bufs[r], p, stream=stream, stages=(stage_map[nm],))
+                evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    t_plain = (time.perf_counter() - t_plain0) / args.steps
+    stage_ms = {nm: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, nm in enumerate(names)}
+    plain_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][-1]) for i in range(args.steps)]))
+
+    # hipGraph: one captured step per replica, replayed in rotation (the timed number)
+    graphs = []
+    for r in range(len(reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            pipeline.run_step(reps[r], bufs[r], p, stream=stream)
+        graphs.append(g)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g0.record(stream)
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+
+    per_stage_bytes, cand, kept = stage_bytes(base, bufs[0], base.d)
+    step_bytes = sum(per_stage_bytes.values())
+    dom = max(per_stage_bytes, key=lambda k: per_stage_bytes[k])
+    achieved = per_stage_bytes[dom] / (stage_ms[dom] * 1e-3)
+    roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK, "traffic": None, "kernel": dom,
+                "bytes_per_launch": per_stage_bytes[dom], "avg_launch_us": stage_ms[dom] * 1e3}
+    step_s = graph_ms * 1e-3
+    res = {
+        "metric": METRIC,
+        "value": cand / step_s,
+        "unit": "candidate tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": graph_ms,
+        "us_per_step": graph_ms * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}: B={spec.B}, Hq={spec.Hq}, Hkv={spec.Hkv}, "
+                               f"head_dim={spec.d}, n={spec.n or spec.n_range}, "
+                               f"Quest budget={w.budget} pages, p={p}",
+                   "config_id": args.config, "p": p, "layer_replicas": len(reps),
+                   "launch": "hipGraph per step"},
+        "hbm_frac_step": step_bytes / step_s / HBM_PEAK,
+        "step_bytes": step_bytes,
+        "candidates": cand,
+        "kept": kept,
+        "plain_launch_us_per_step": plain_ms * 1e3,
+        "host_us_per_plain_step": t_plain * 1e6,
+        "stage_us_plain": {k: v * 1e3 for k, v in stage_ms.items()},
+        "stage_bytes": per_stage_bytes,
+        "cache_build_ms": build_ms,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, p, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle, through the C ABI.
+
+Small versions of the five workloads (same head layout, planting recipe and paging, shorter
+contexts and ragged tails) are checked unit by unit and stage by stage; the acceptance
+rules are in tests/parity.py. Full-size runs live in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from adaptive_top_sparse_amd import workloads  # noqa: E402
+from tests import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "cfg1": (1, {}, 0.9),
+    "cfg2s": (2, dict(n=2048 + 7, budget=32), 0.85),
+    "cfg3s": (3, dict(n=8192 + 5, budget=64), 0.9),
+    "cfg4s": (4, dict(B=4, n_range=(40, 3000), budget=32), 0.85),
+    "cfg5s-p0.8": (5, dict(B=2, n=4096), 0.8),
+    "cfg5s-p0.9": (5, dict(B=2, n=4096), 0.9),
+    "cfg5s-p0.95": (5, dict(B=2, n=4096), 0.95),
+}
+
+
+def _run(w, p, repeat=1):
+    from adaptive_top_sparse_amd import pipeline
+    c = pipeline.upload(w)
+    c.build_caches()
+    buf = pipeline.alloc_step(c)
+    outs = []
+    for _ in range(repeat):
+        pipeline.run_step(c, buf, p)
+        torch.cuda.synchronize()
+        outs.append({k: (None if v is None else v.cpu().numpy().copy())
+                     for k, v in vars(buf).items() if k != "workspace"})
+    host = {
+        "k_codes": c.k_codes.cpu().numpy(),
+        "k_meta": c.k_meta.cpu().numpy(),
+        "page_minmax": None if c.page_minmax is None else c.page_minmax.cpu().numpy(),
+    }
+    return c, host, outs
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def case(request):
+    cfg, over, p = CASES[request.param]
+    print(f"\n[parity case] {request.param} cfg={cfg} {over} p={p}", flush=True)
+    w = workloads.make_workload(cfg, **over)
+    c, host, outs = _run(w, p, repeat=2)
+    orc = parity.oracle_units(w, p)
+    return dict(name=request.param, w=w, p=p, host=host, out=outs[0], out2=outs[1], orc=orc)
+
+
+def test_quantized_keys_bit_exact(case):
+    w, host, orc = case["w"], case["host"], case["orc"]
+    for (b, g), res in orc.items():
+        n = int(w.seq_lens[b])
+        if n == 0:
+            continue
+        codes = parity.unpack_codes(parity.logical_rows(host["k_codes"], w.page_table[b], n, g))
+        assert np.array_equal(codes, res["codes"]), (b, g)
+        meta = parity.logical_rows(host["k_meta"], w.page_table[b], n, g)
+        assert np.array_equal(meta[..., 0].astype(np.float64), res["scale"].astype(np.float64))
+        assert np.array_equal(meta[..., 1].astype(np.float64), res["zero"].astype(np.float64))
+
+
+def test_page_bounds_bit_exact(case):
+    w, host, orc = case["w"], case["host"], case["orc"]
+    if host["page_minmax"] is None:
+        pytest.skip("no page selector in this workload")
+    for (b, g), res in orc.items():
+        n = int(w.seq_lens[b])
+        P = -(-n // 16)
+        mm = host["page_minmax"][w.page_table[b, :P], g]          # [P, 2, d]
+        assert np.array_equal(mm[:, 0].astype(np.float64), res["lo"].astype(np.float64)), (b, g)
+        assert np.array_equal(mm[:, 1].astype(np.float64), res["hi"].astype(np.float64)), (b, g)
+
+
+def test_quest_pages_bit_exact(case):
+    w, out, orc = case["w"], case["out"], case["orc"]
+    if out["sel_pages"] is None:
+        pytest.skip("no page selector in this workload")
+    for (b, g), res in orc.items():
+        cnt = int(out["sel_count"][b, g])
+        assert cnt == len(res["sel"]), (b, g)
+        assert np.array_equal(out["sel_pages"][b, g, :cnt], res["sel"]), (b, g)
+
+
+def test_estimated_weights(case):
+    w, out, orc = case["w"], case["out"], case["orc"]
+    G = w.spec.G
+    worst = 0.0
+    for (b, g), res in orc.items():
+        wg = out["weights"][b, g * G:(g + 1) * G]
+        worst = max(worst, parity.check_weights(wg, res["weights"], res["valid"]))
+    print(f"[{case['name']}] worst weight rel err {worst:.2e}")
+
+
+def test_topp_kept_sets(case):
+    w, out, orc, p = case["w"], case["out"], case["orc"], case["p"]
+    ndiff = 0
+    for (b, g), res in orc.items():
+        n = int(w.seq_lens[b])
+        cnt = int(out["kept_count"][b, g])
+        kept = out["kept"][b, g, :cnt]
+        _, d = parity.check_kept(kept, res, p, n)
+        ndiff += d
+    print(f"[{case['name']}] kept-set differences at tau: {ndiff}")
+
+
+def test_sparse_decode(case):
+    w, out, orc = case["w"], case["out"], case["orc"]
+    G = w.spec.G
+    sm = parity.sm_scale_for(w.spec.d)
+    worst = (0.0, 0.0)
+    for (b, g), res in orc.items():
+        cnt = int(out["kept_count"][b, g])
+        kept = out["kept"][b, g, :cnt]
+        o = out["out"][b, g * G:(g + 1) * G]
+        e = parity.check_out(o, w.q[b, g * G:(g + 1) * G], w.k[b][g], w.v[b][g], kept, res, sm)
+        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+    print(f"[{case['name']}] worst decode err {worst[0]:.2e}, end-to-end {worst[1]:.2e}")
+
+
+def test_repeat_is_bit_identical(case):
+    a, b = case["out"], case["out2"]
+    for key in a:
+        if a[key] is None:
+            continue
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
