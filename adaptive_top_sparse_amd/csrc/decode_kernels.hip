@@ -3,23 +3,51 @@
 // the tokens that survive pruning).
 //
 // For each query head h of KV head g: o_h = sum_{j in kept} softmax_j(sm_scale q_h . k_j) v_j
-// on the fp16 cache, the softmax over the kept set only. Split-KV: each work-group takes a
-// chunk of the kept list and leaves (max, sum, unnormalized o) in log2 units; a merge kernel
-// combines the chunks and rounds to fp16.
+// on the fp16 cache, the softmax over the kept set only.
 //
-// Layout on the device: D/8 lanes per kept token, 8 channels (16 B of K, 16 B of V) per lane,
-// so one wave gathers 64/(D/8) token rows per load instruction, each row one contiguous
-// 2*D-byte stretch of the paged cache. q . k uses v_dot2_f32_f16 on fp16 pairs (exact
-// products, fp32 sums); the softmax and p * v run in fp32.
+// Split-KV: each work-group takes a chunk of a KV head's kept list and leaves (max, sum,
+// unnormalized o) in log2 units in the workspace; a merge kernel combines the chunks and
+// writes the fp16 output. A list that fits one chunk is finished in place. (Merging in the
+// last work-group to finish, found with an atomic ticket, needs device-scope fences that
+// write back and invalidate whole L2s on this multi-XCD part; measured, it costs far more
+// than the second launch.)
+//
+// Layout on the device: D/8 lanes per kept token, 8 channels (16 B of K, 16 B of V) per
+// lane, so one wave gathers 64/(D/8) token rows per load instruction, each row one
+// contiguous 2*D-byte stretch of the paged cache. q . k uses v_dot2_f32_f16 on fp16 pairs
+// (exact products, fp32 sums) reduced across the row's lanes with DPP; softmax and p * v run
+// in fp32.
 #include "twl_device.h"
 #include "twl_launch.h"
+
+TWL_PHASE_STORAGE(decode)
+TWL_SPAN_STORAGE(decode)
 
 namespace twl {
 namespace {
 
-constexpr int kDecThreads = 256;
+// Tuning constants (compile-time; the defaults are the measured choice on MI355X).
+#ifndef TWL_DEC_THREADS
+#define TWL_DEC_THREADS 256
+#endif
+#ifndef TWL_DEC_UNROLL
+#define TWL_DEC_UNROLL 4
+#endif
+#ifndef TWL_DEC_TARGET_BLOCKS
+#define TWL_DEC_TARGET_BLOCKS 512
+#endif
+#ifndef TWL_DEC_MIN_CHUNK
+#define TWL_DEC_MIN_CHUNK 64
+#endif
+constexpr int kDecThreads = TWL_DEC_THREADS;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kDecUnroll = 4;
+constexpr int kDecUnroll = TWL_DEC_UNROLL;
+constexpr int kDecMaxChunks = 256;  // per KV head; the merge holds (m, l) of each in LDS
+#ifndef TWL_DEC_MAX_CHUNK
+#define TWL_DEC_MAX_CHUNK 512
+#endif
+constexpr int kDecMaxChunkTokens = TWL_DEC_MAX_CHUNK;  // kept tokens per work-group, at most
+constexpr int kMergeSlice = 16;     // channels per merge work-group
 
 __device__ __forceinline__ float rescale(float m, float M) {
   return m == -INFINITY ? 0.f : exp2f(m - M);
@@ -28,40 +56,67 @@ __device__ __forceinline__ float rescale(float m, float M) {
 __device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
 template <int D, int G>
-__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
+__global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ kept_count, int kept_stride, int Hkv, int max_pages,
-    int num_phys, float scale_log2, float* __restrict__ partials, int n_chunks,
-    int chunk_tokens) {
-  constexpr int LPT = D / 8;      // lanes per token row
+    int num_phys, float scale_log2, float* __restrict__ partials,
+    int n_chunks, int chunk_tokens, uint16_t* __restrict__ out) {
+  constexpr int LPT = D / 8;        // lanes per token row
   constexpr int TPW = kWave / LPT;  // token rows per wave per load
   constexpr int STEP = TPW * kDecUnroll;
+  constexpr int PSTRIDE = D + 4;    // floats per (chunk, head) partial: m, l, 2 pad, o[D]
   __shared__ float s_m[kDecWaves][G], s_l[kDecWaves][G];
   __shared__ float s_acc[kDecWaves][G][D];
+  __shared__ long s_row[kDecMaxChunkTokens];
+  TWL_PHASE(0);
+  TWL_SPAN_BEGIN();
 
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int chunk = blockIdx.x;
   const long unit = static_cast<long>(b) * Hkv + g;
+  const int Hq = Hkv * G;
   int K = kept_count[unit];
   K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
+  const int nc = (K + chunk_tokens - 1) / chunk_tokens;
+  const long head0 = static_cast<long>(b) * Hq + g * G;
+  if (K == 0) {
+    // empty kept set: o = 0, written by the first work-group
+    if (chunk == 0)
+      for (int i = threadIdx.x; i < G * D; i += kDecThreads) out[head0 * D + i] = 0;
+    return;
+  }
   const int t0 = chunk * chunk_tokens;
   if (t0 >= K) return;
   const int t1 = min(K, t0 + chunk_tokens);
   const int n = seq_len_clamped(seq_lens, b, max_pages);
-  const int Hq = Hkv * G;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int sub = lane % LPT;
   const int tk = lane / LPT;
   const int c0 = sub * 8;
 
+  // the chunk's kept ids -> element offsets of their cache rows (-1: absent), once
+  {
+    const int32_t* krow = kept + unit * kept_stride;
+    const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
+    for (int i = threadIdx.x; i < t1 - t0; i += kDecThreads) {
+      const int tok = krow[t0 + i];
+      long row = -1;
+      if (tok >= 0 && tok < n) {
+        const int phys = trow[tok / kPage];
+        if (phys_ok(phys, num_phys))
+          row = ((static_cast<long>(phys) * Hkv + g) * kPage + tok % kPage) * D;
+      }
+      s_row[i] = row;
+    }
+  }
   uint32_t qw[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q + (static_cast<long>(b) * Hq + g * G + h) * D + c0);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q + (head0 + h) * D + c0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) qw[h][j] = v[j];
   }
@@ -73,29 +128,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
   }
-  const int32_t* krow = kept + unit * kept_stride;
-  const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
+  __syncthreads();
 
-  for (int base = t0 + wave * STEP; base < t1; base += kDecWaves * STEP) {
-    u32x4 kv[kDecUnroll], vv[kDecUnroll];
-    bool ok[kDecUnroll];
+  // this wave's batches: token slots base + u*TPW + tk, base stepping by all waves' batches
+  const int n_tok = t1 - t0;
+  auto load_batch = [&](int base, long (&row)[kDecUnroll], u32x4 (&kv)[kDecUnroll],
+                        u32x4 (&vv)[kDecUnroll]) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int t = base + u * TPW + tk;
-      int tok = t < t1 ? krow[t] : -1;
-      bool good = tok >= 0 && tok < n;
-      const int phys = good ? trow[tok / kPage] : -1;
-      good = good && phys_ok(phys, num_phys);
-      ok[u] = good;
-      if (good) {
-        const long row = ((static_cast<long>(phys) * Hkv + g) * kPage + tok % kPage) * D + c0;
-        kv[u] = *reinterpret_cast<const u32x4*>(k_cache + row);
-        vv[u] = *reinterpret_cast<const u32x4*>(v_cache + row);
+      row[u] = t < n_tok ? s_row[t] : -1;
+      if (row[u] >= 0) {
+        kv[u] = *reinterpret_cast<const u32x4*>(k_cache + row[u] + c0);
+        vv[u] = *reinterpret_cast<const u32x4*>(v_cache + row[u] + c0);
       } else {
         kv[u] = u32x4{0u, 0u, 0u, 0u};
         vv[u] = u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  long row[kDecUnroll];
+  u32x4 kv[kDecUnroll], vv[kDecUnroll];
+  int base = wave * STEP;
+  if (base < n_tok) load_batch(base, row, kv, vv);
+  for (; base < n_tok; base += kDecWaves * STEP) {
+    // prefetch the next batch before computing this one
+    long row_n[kDecUnroll];
+    u32x4 kv_n[kDecUnroll], vv_n[kDecUnroll];
+    const int next = base + kDecWaves * STEP;
+    if (next < n_tok) load_batch(next, row_n, kv_n, vv_n);
+
     float s[kDecUnroll][G];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
@@ -105,60 +167,62 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           d = __builtin_amdgcn_fdot2(as_h2(qw[h][j]), as_h2(kv[u][j]), d, false);
-#pragma unroll
-        for (int o = LPT / 2; o > 0; o >>= 1) d += __shfl_xor(d, o);
-        s[u][h] = ok[u] ? d * scale_log2 : -INFINITY;
+        d = group_sum<LPT>(d);
+        s[u][h] = row[u] >= 0 ? d * scale_log2 : -INFINITY;
       }
     }
-    float vf[kDecUnroll][8];
-#pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x2 p2 = as_h2(vv[u][j]);
-        vf[u][2 * j] = static_cast<float>(p2[0]);
-        vf[u][2 * j + 1] = static_cast<float>(p2[1]);
-      }
-    }
+    // one running max per head for the whole wave: the token groups' batch maxima are
+    // combined across groups, so every group's (l, acc) stays on the same scale
+    float pr[kDecUnroll][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mb = s[0][h];
 #pragma unroll
       for (int u = 1; u < kDecUnroll; ++u) mb = fmaxf(mb, s[u][h]);
+      mb = across_groups<LPT>(mb, OpMax());
       const float mn = fmaxf(m[h], mb);
-      if (mn == -INFINITY) continue;
       const float alpha = rescale(m[h], mn);
-      l[h] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] *= alpha;
+      float lsum = l[h] * alpha;
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) {
-        const float pr = rescale(s[u][h], mn);
-        l[h] += pr;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(pr, vf[u][c], acc[h][c]);
+        pr[u][h] = mn == -INFINITY ? 0.f : rescale(s[u][h], mn);
+        lsum += pr[u][h];
       }
+      l[h] = lsum;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] *= alpha;
       m[h] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      float vf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2 p2 = as_h2(vv[u][j]);
+        vf[2 * j] = static_cast<float>(p2[0]);
+        vf[2 * j + 1] = static_cast<float>(p2[1]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(pr[u][h], vf[c], acc[h][c]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      row[u] = row_n[u];
+      kv[u] = kv_n[u];
+      vv[u] = vv_n[u];
     }
   }
 
-  // merge the TPW token lanes of each channel slice inside the wave
+  TWL_PHASE(1);
+  // sum the token groups of each channel slice (same scale: m is shared by the wave)
 #pragma unroll
-  for (int o = LPT; o < kWave; o <<= 1) {
+  for (int h = 0; h < G; ++h) {
+    l[h] = across_groups<LPT>(l[h], OpSum());
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], o);
-      const float lo = __shfl_xor(l[h], o);
-      const float M = fmaxf(m[h], mo);
-      const float a = rescale(m[h], M), bb = rescale(mo, M);
-      l[h] = l[h] * a + lo * bb;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float ao = __shfl_xor(acc[h][c], o);
-        acc[h][c] = acc[h][c] * a + ao * bb;
-      }
-      m[h] = M;
-    }
+    for (int c = 0; c < 8; ++c) acc[h][c] = across_groups<LPT>(acc[h][c], OpSum());
   }
   if (tk == 0) {
 #pragma unroll
@@ -172,6 +236,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
     }
   }
   __syncthreads();
+  TWL_PHASE(2);
+  // this chunk's (M, L, A) per head, merged over the waves
   for (int i = threadIdx.x; i < G * D; i += kDecThreads) {
     const int h = i / D, c = i % D;
     float M = s_m[0][h];
@@ -184,78 +250,136 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
       L += s_l[w][h] * f;
       A += s_acc[w][h][c] * f;
     }
-    float* dst = partials + ((static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk) * (D + 2);
-    if (c == 0) {
-      dst[0] = M;
-      dst[1] = L;
+    if (nc == 1) {
+      const float o = L > 0.f ? A / L : 0.f;
+      out[(head0 + h) * D + c] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
+    } else {
+      float* dst = partials + ((head0 + h) * n_chunks + chunk) * PSTRIDE;
+      if (c == 0) {
+        dst[0] = M;
+        dst[1] = L;
+      }
+      dst[4 + c] = A;
     }
-    dst[2 + c] = A;
   }
+  TWL_PHASE(3);
+  TWL_SPAN_END();
 }
 
-// One work-group of D threads per (sequence, query head): lane c merges channel c.
+// Merge of the chunk partials when they are more than one: one wave per (sequence, query
+// head, 16-channel slice). Lanes take chunks; every load is independent, so the whole merge
+// is about two memory round trips.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
+__global__ __launch_bounds__(kWave) void decode_merge_kernel(
     const float* __restrict__ partials, const int32_t* __restrict__ kept_count, int kept_stride,
     int Hkv, int G, int n_chunks, int chunk_tokens, uint16_t* __restrict__ out) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  constexpr int PSTRIDE = D + 4;
+  constexpr int PER = kDecMaxChunks / kWave;  // chunks per lane at most
+  __shared__ float s_acc[kWave][kMergeSlice + 1];
+  const int slice = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
   const int Hq = Hkv * G;
   const long unit = static_cast<long>(b) * Hkv + h / G;
   int K = kept_count[unit];
   K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
   const int nc = (K + chunk_tokens - 1) / chunk_tokens;
-  const int c = threadIdx.x;
-  const float* pr = partials + (static_cast<long>(b) * Hq + h) * n_chunks * (D + 2);
-  float M = -INFINITY;
-  for (int i = 0; i < nc; ++i) M = fmaxf(M, pr[i * (D + 2)]);
-  float L = 0.f, A = 0.f;
-  for (int i = 0; i < nc; ++i) {
-    const float f = rescale(pr[i * (D + 2)], M);
-    L += pr[i * (D + 2) + 1] * f;
-    A += pr[i * (D + 2) + 2 + c] * f;
+  if (nc <= 1) return;  // finished by the partial kernel
+  const int lane = lane_id();
+  const float* ph = partials + (static_cast<long>(b) * Hq + h) * n_chunks * PSTRIDE;
+  float mi[PER], li[PER];
+  f32x4 a[PER][kMergeSlice / 4];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = lane + k * kWave;
+    const bool ok = i < nc;
+    const float* pi = ph + static_cast<long>(i) * PSTRIDE;
+    mi[k] = ok ? pi[0] : -INFINITY;
+    li[k] = ok ? pi[1] : 0.f;
+#pragma unroll
+    for (int v = 0; v < kMergeSlice / 4; ++v) {
+      if (ok) {
+        a[k][v] = *reinterpret_cast<const f32x4*>(pi + 4 + slice * kMergeSlice + 4 * v);
+      } else {
+        a[k][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
   }
-  const float o = L > 0.f ? A / L : 0.f;
-  out[(static_cast<long>(b) * Hq + h) * D + c] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
+  float M = mi[0];
+#pragma unroll
+  for (int k = 1; k < PER; ++k) M = fmaxf(M, mi[k]);
+  M = wave_max(M);
+  float L = 0.f;
+  float acc[kMergeSlice];
+#pragma unroll
+  for (int c = 0; c < kMergeSlice; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const float f = rescale(mi[k], M);
+    L = fmaf(li[k], f, L);
+#pragma unroll
+    for (int v = 0; v < kMergeSlice / 4; ++v) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[4 * v + j] = fmaf(a[k][v][j], f, acc[4 * v + j]);
+    }
+  }
+  L = wave_sum(L);
+#pragma unroll
+  for (int c = 0; c < kMergeSlice; ++c) s_acc[lane][c] = acc[c];
+  __syncthreads();
+  if (lane < kMergeSlice) {
+    float t = 0.f;
+    for (int r = 0; r < kWave; ++r) t += s_acc[r][lane];
+    const float o = L > 0.f ? t / L : 0.f;
+    out[(static_cast<long>(b) * Hq + h) * D + slice * kMergeSlice + lane] =
+        __builtin_bit_cast(uint16_t, static_cast<f16>(o));
+  }
 }
 
 template <int D, int G>
-void partial_launch(const Layout& L, const void* q, const void* k, const void* v,
-                    const int32_t* kept, const int32_t* kept_count, int kept_stride,
-                    float scale_log2, float* partials, int n_chunks, int ch, hipStream_t s) {
-  decode_partial_kernel<D, G><<<dim3(n_chunks, L.Hkv, L.B), kDecThreads, 0, s>>>(
+void decode_launch(const Layout& L, const void* q, const void* k, const void* v,
+                   const int32_t* kept, const int32_t* kept_count, int kept_stride,
+                   float scale_log2, float* partials, int n_chunks, int ch, void* out,
+                   hipStream_t s) {
+  sparse_decode_kernel<D, G><<<dim3(n_chunks, L.Hkv, L.B), kDecThreads, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), L.page_table, L.seq_lens, kept, kept_count, kept_stride,
-      L.Hkv, L.max_pages, L.num_phys, scale_log2, partials, n_chunks, ch);
+      L.Hkv, L.max_pages, L.num_phys, scale_log2, partials, n_chunks, ch,
+      static_cast<uint16_t*>(out));
 }
 
 template <int D>
-void partial_dispatch_g(const Layout& L, const void* q, const void* k, const void* v,
-                        const int32_t* kept, const int32_t* kept_count, int kept_stride,
-                        float scale_log2, float* partials, int n_chunks, int ch, hipStream_t s) {
+void decode_dispatch_g(const Layout& L, const void* q, const void* k, const void* v,
+                       const int32_t* kept, const int32_t* kept_count, int kept_stride,
+                       float scale_log2, float* partials, int n_chunks, int ch, void* out,
+                       hipStream_t s) {
   switch (L.G()) {
-    case 1: partial_launch<D, 1>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, s); break;
-    case 2: partial_launch<D, 2>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, s); break;
-    case 4: partial_launch<D, 4>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, s); break;
-    default: partial_launch<D, 8>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, s); break;
+    case 1: decode_launch<D, 1>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
+    case 2: decode_launch<D, 2>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
+    case 4: decode_launch<D, 4>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
+    default: decode_launch<D, 8>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
   }
 }
 
 }  // namespace
 
 int decode_chunk_tokens(const Layout& L, int kept_stride) {
-  // aim at about 2048 work-groups over the largest possible kept lists
+  // about TWL_DEC_TARGET_BLOCKS work-groups over the largest possible kept lists, at most
+  // kDecMaxChunks chunks per KV head, at most kDecMaxChunkTokens tokens per chunk
   const long units = static_cast<long>(L.B) * L.Hkv;
-  long ch = (static_cast<long>(kept_stride) * units + 2047) / 2048;
-  long c = 64;
-  while (c < ch && c < 2048) c <<= 1;
+  const long by_blocks =
+      (static_cast<long>(kept_stride) * units + TWL_DEC_TARGET_BLOCKS - 1) / TWL_DEC_TARGET_BLOCKS;
+  const long by_merge = (static_cast<long>(kept_stride) + kDecMaxChunks - 1) / kDecMaxChunks;
+  const long want = by_blocks > by_merge ? by_blocks : by_merge;
+  long c = TWL_DEC_MIN_CHUNK;
+  while (c < want && c < kDecMaxChunkTokens) c <<= 1;
   return static_cast<int>(c);
 }
 
 size_t decode_workspace_bytes(const Layout& L, int kept_stride) {
   const int ch = decode_chunk_tokens(L, kept_stride);
   const long n_chunks = (static_cast<long>(kept_stride) + ch - 1) / ch;
-  return align_up(static_cast<size_t>(L.B) * L.Hq * n_chunks * (L.d + 2) * sizeof(float), 256);
+  return align_up(static_cast<size_t>(L.B) * L.Hq * n_chunks * (L.d + 4) * sizeof(float), 256);
 }
 
 hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_cache,
@@ -264,24 +388,25 @@ hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_ca
                                 void* out, void* ws, hipStream_t s) {
   const int ch = decode_chunk_tokens(L, kept_stride);
   const int n_chunks = (kept_stride + ch - 1) / ch;
-  float* partials = static_cast<float*>(ws);
+  auto* partials = static_cast<float*>(stage_scratch(ws, L));
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (L.d == 128) {
-    partial_dispatch_g<128>(L, q, k_cache, v_cache, kept, kept_count, kept_stride, scale_log2,
-                            partials, n_chunks, ch, s);
+    decode_dispatch_g<128>(L, q, k_cache, v_cache, kept, kept_count, kept_stride, scale_log2,
+                           partials, n_chunks, ch, out, s);
   } else {
-    partial_dispatch_g<64>(L, q, k_cache, v_cache, kept, kept_count, kept_stride, scale_log2,
-                           partials, n_chunks, ch, s);
+    decode_dispatch_g<64>(L, q, k_cache, v_cache, kept, kept_count, kept_stride, scale_log2,
+                          partials, n_chunks, ch, out, s);
   }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto* o = static_cast<uint16_t*>(out);
+  const dim3 grid(L.d / kMergeSlice, L.Hq, L.B);
   if (L.d == 128) {
-    decode_merge_kernel<128><<<dim3(L.Hq, L.B), 128, 0, s>>>(partials, kept_count, kept_stride,
-                                                             L.Hkv, L.G(), n_chunks, ch, o);
+    decode_merge_kernel<128><<<grid, kWave, 0, s>>>(partials, kept_count, kept_stride, L.Hkv,
+                                                    L.G(), n_chunks, ch, o);
   } else {
-    decode_merge_kernel<64><<<dim3(L.Hq, L.B), 64, 0, s>>>(partials, kept_count, kept_stride,
-                                                           L.Hkv, L.G(), n_chunks, ch, o);
+    decode_merge_kernel<64><<<grid, kWave, 0, s>>>(partials, kept_count, kept_stride, L.Hkv,
+                                                   L.G(), n_chunks, ch, o);
   }
   return hipGetLastError();
 }

@@ -11,6 +11,8 @@
 #include "twl_device.h"
 #include "twl_launch.h"
 
+TWL_PHASE_STORAGE(estimate)
+
 namespace twl {
 namespace {
 
@@ -29,6 +31,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   __shared__ float qs[G][D];
   __shared__ float qsum[G][NG];
   __shared__ float red[kEstChunk / kWave];
+  TWL_PHASE(0);
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -65,6 +68,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       }
     }
   }
+  TWL_PHASE(1);
   bool valid = tok >= 0 && tok < n;
   float s[G];
 #pragma unroll
@@ -116,16 +120,41 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       for (int h = 0; h < G; ++h) s[h] = sm_scale * acc[h];
     }
   }
-  // logits row, then (max, sum exp) of this chunk per head
+  // logits row, then (max, sum exp) of this chunk per head: one max pass and one sum pass
+  // for all G heads
+  __shared__ float red_m[kEstChunk / kWave][G], red_l[kEstChunk / kWave][G];
+  const int wave = threadIdx.x / kWave;
+  TWL_PHASE(2);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const long hrow = static_cast<long>(b) * Hq + g * G + h;
     if (slot < n_slots) logits[hrow * n_slots + slot] = s[h];
-    const float m = block_max<kEstChunk>(s[h], red);
-    const float e = (valid && m > -INFINITY) ? expf(s[h] - m) : 0.f;
-    const float l = block_sum<kEstChunk>(e, red);
-    if (threadIdx.x == 0) partials[hrow * n_chunks + chunk] = make_float2(m, l);
+    const float wm = wave_max(s[h]);
+    if (lane_id() == 0) red_m[wave][h] = wm;
   }
+  __syncthreads();
+  float e[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = red_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kEstChunk / kWave; ++w) m = fmaxf(m, red_m[w][h]);
+    e[h] = (valid && m > -INFINITY) ? expf(s[h] - m) : 0.f;
+    const float ws = wave_sum(e[h]);
+    if (lane_id() == 0) red_l[wave][h] = ws;
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float m = red_m[0][h], l = 0.f;
+#pragma unroll
+    for (int w = 1; w < kEstChunk / kWave; ++w) m = fmaxf(m, red_m[w][h]);
+#pragma unroll
+    for (int w = 0; w < kEstChunk / kWave; ++w) l += red_l[w][h];
+    const long hrow = static_cast<long>(b) * Hq + g * G + h;
+    partials[hrow * n_chunks + chunk] = make_float2(m, l);
+  }
+  TWL_PHASE(3);
 }
 
 // w = exp(s - M) / L with (M, L) merged from the row's chunk partials; invalid slots hold
@@ -134,22 +163,23 @@ __global__ __launch_bounds__(kEstChunk) void estimate_normalize_kernel(
     float* __restrict__ weights, const float2* __restrict__ partials, int n_chunks, int n_slots) {
   __shared__ float red[kEstChunk / kWave];
   const long hrow = static_cast<long>(blockIdx.y) * gridDim.z + blockIdx.z;
+  const int slot = blockIdx.x * kEstChunk + threadIdx.x;
+  float* w = weights + hrow * n_slots + slot;
+  const float s = slot < n_slots ? *w : -INFINITY;  // issued before the partials
   const float2* pr = partials + hrow * n_chunks;
-  float m = -INFINITY;
-  for (int i = threadIdx.x; i < n_chunks; i += blockDim.x) m = fmaxf(m, pr[i].x);
-  const float M = block_max<kEstChunk>(m, red);
-  float l = 0.f;
-  if (M > -INFINITY) {
-    for (int i = threadIdx.x; i < n_chunks; i += blockDim.x) {
-      const float2 v = pr[i];
-      if (v.x > -INFINITY) l += v.y * expf(v.x - M);
+  float m = -INFINITY, l = 0.f;
+  // this thread's share of the chunk partials, merged on the fly
+  for (int i = threadIdx.x; i < n_chunks; i += blockDim.x) {
+    const float2 v = pr[i];
+    if (v.x > -INFINITY) {
+      const float mn = fmaxf(m, v.x);
+      l = (m > -INFINITY ? l * expf(m - mn) : 0.f) + v.y * expf(v.x - mn);
+      m = mn;
     }
   }
-  const float L = block_sum<kEstChunk>(l, red);
-  const int slot = blockIdx.x * kEstChunk + threadIdx.x;
+  const float M = block_max<kEstChunk>(m, red);
+  const float L = block_sum<kEstChunk>(m > -INFINITY ? l * expf(m - M) : 0.f, red);
   if (slot >= n_slots) return;
-  float* w = weights + hrow * n_slots + slot;
-  const float s = *w;
   *w = (L > 0.f && s > -INFINITY) ? expf(s - M) / L : 0.f;
 }
 
@@ -191,7 +221,7 @@ hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes,
                            hipStream_t s) {
   const int n_slots = cand_stride_pages * kPage;
   const int n_chunks = (n_slots + kEstChunk - 1) / kEstChunk;
-  float2* partials = static_cast<float2*>(ws);
+  float2* partials = static_cast<float2*>(stage_scratch(ws, L));
   if (L.d == 128) {
     logits_dispatch_g<128>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
                            sm_scale, weights, partials, n_chunks, s);

@@ -13,19 +13,25 @@
 #include "twl_device.h"
 #include "twl_launch.h"
 
+TWL_PHASE_STORAGE(quest)
+
 namespace twl {
 namespace {
 
 constexpr int kScorePagesPerBlock = 64;
 
-// Lanes per page = D/8 (each lane owns 8 channels = 16 B of lo and 16 B of hi).
+// Lanes per page = D/8 (each lane owns 8 channels = 16 B of lo and 16 B of hi). A block of
+// 256 threads covers 256/LPP pages per round and all rounds' page ids and bounds are
+// loaded before any arithmetic, so each lane has 2 * ROUNDS loads in flight.
 template <int D>
 __global__ __launch_bounds__(256) void quest_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ minmax,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int Hq,
     int Hkv, int max_pages, int num_phys, double* __restrict__ scores) {
   constexpr int LPP = D / 8;
-  constexpr int PPI = 256 / LPP;  // pages per block iteration
+  constexpr int PPI = 256 / LPP;  // pages per round
+  constexpr int ROUNDS = kScorePagesPerBlock / PPI;
+  TWL_PHASE(0);
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int G = Hq / Hkv;
@@ -35,7 +41,27 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   if (p0 >= P) return;
   const int sub = threadIdx.x % LPP;
   const int c0 = sub * 8;
+  const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
 
+  int phys[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int p = p0 + r * PPI + threadIdx.x / LPP;
+    phys[r] = p < P ? trow[p] : -1;
+    if (!phys_ok(phys[r], num_phys)) phys[r] = -1;
+  }
+  u32x4 lo[ROUNDS], hi[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    if (phys[r] >= 0) {
+      const uint16_t* blk = minmax + (static_cast<long>(phys[r]) * Hkv + g) * 2 * D + c0;
+      lo[r] = *reinterpret_cast<const u32x4*>(blk);
+      hi[r] = *reinterpret_cast<const u32x4*>(blk + D);
+    } else {
+      lo[r] = u32x4{0u, 0u, 0u, 0u};
+      hi[r] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   double A[8], Bc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -52,43 +78,43 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
       if (x < 0.0) A[c] += x; else Bc[c] += x;
     }
   }
-
+  TWL_PHASE(1);
   double* out = scores + (static_cast<long>(b) * Hkv + g) * max_pages;
-  const int p_end = min(P, p0 + kScorePagesPerBlock);
-  // the LPP lanes of a page group share p and trip count, so the shuffles stay in-group
-  for (int p = p0 + threadIdx.x / LPP; p < p_end; p += PPI) {
-    double acc = 0.0;
-    const int phys = page_table[static_cast<long>(b) * max_pages + p];
-    if (phys_ok(phys, num_phys)) {
-      const uint16_t* blk = minmax + (static_cast<long>(phys) * Hkv + g) * 2 * D + c0;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(blk);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(blk + D);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int sh = 16 * (c % 2);
-        const double l = static_cast<double>(h2f(static_cast<uint16_t>((lo[c / 2] >> sh) & 0xffffu)));
-        const double u = static_cast<double>(h2f(static_cast<uint16_t>((hi[c / 2] >> sh) & 0xffffu)));
-        acc = fma(l, A[c], acc);
-        acc = fma(u, Bc[c], acc);
-      }
+  for (int r = 0; r < ROUNDS; ++r) {
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int sh = 16 * (c % 2);
+      const double l = static_cast<double>(h2f(static_cast<uint16_t>((lo[r][c / 2] >> sh) & 0xffffu)));
+      const double u = static_cast<double>(h2f(static_cast<uint16_t>((hi[r][c / 2] >> sh) & 0xffffu)));
+      acc = fma(l, A[c], acc);
+      acc = fma(u, Bc[c], acc);
     }
 #pragma unroll
     for (int o = LPP / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (sub == 0) out[p] = acc;
+    const int p = p0 + r * PPI + threadIdx.x / LPP;
+    if (sub == 0 && p < P) out[p] = acc;
   }
+  TWL_PHASE(2);
 }
 
-// One 1024-thread block per (sequence, KV head). Thread t owns pages [t*KPT, t*KPT+KPT).
-// Radix select over order-preserving 64-bit keys of the exact scores, 8 bits per pass from
-// the top, stopping as soon as the boundary digit's bucket is taken whole; remaining exact
-// ties are resolved by page index. Then a block scan compacts the chosen pages in order.
+// One 1024-thread block per (sequence, KV head); thread t owns pages [t*KPT, t*KPT+KPT).
+// Radix select over order-preserving 64-bit keys of the exact scores: the bits the keys
+// all share are skipped (block min/max), then 11-bit digits are examined from the top,
+// stopping as soon as the boundary bucket is taken whole; remaining exact ties go to the
+// lower page index. A block scan then compacts the chosen pages in page order.
 template <int KPT>
 __global__ __launch_bounds__(1024) void quest_select_kernel(
     const double* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv,
     int max_pages, int budget, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_lds[1024 / kWave + 1];
+  constexpr int NT = 1024;
+  constexpr int kBins = 2 * NT;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t scan_lds[NT / kWave + 1];
+  __shared__ uint64_t red64[NT / kWave];
   __shared__ uint32_t pick[3];
+  TWL_PHASE(4);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
   const int n = seq_len_clamped(seq_lens, b, max_pages);
@@ -98,61 +124,62 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   int32_t* out = sel_pages + unit * budget;
   if (threadIdx.x == 0) sel_count[unit] = m;
   if (m == P) {
-    for (int i = threadIdx.x; i < P; i += blockDim.x) out[i] = i;
+    for (int i = threadIdx.x; i < P; i += NT) out[i] = i;
     return;
   }
   const double* sc = scores + unit * max_pages;
   const int first = threadIdx.x * KPT;
   uint64_t key[KPT];
+  uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int p = first + i;
     key[i] = p < P ? f64_order_key(sc[p]) : 0ull;
+    if (p < P) {
+      kmin = key[i] < kmin ? key[i] : kmin;
+      kmax = key[i] > kmax ? key[i] : kmax;
+    }
   }
+  TWL_PHASE(5);
+  kmin = block_min_u64<NT>(kmin, red64);
+  kmax = block_max_u64<NT>(kmax, red64);
+  TWL_PHASE(6);
 
-  uint64_t prefix = 0, mask = 0;
+  // bits above `top` are common to every key
+  uint64_t prefix, mask;
   uint32_t rem = static_cast<uint32_t>(m);
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-    __syncthreads();
+  if (kmin == kmax) {
+    prefix = kmax;
+    mask = ~0ull;
+  } else {
+    int top = 63 - __clzll(kmin ^ kmax);
+    mask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
+    prefix = kmax & mask;
+    int npass = 0;
+    for (;;) {
+      const int lo_bit = top >= 10 ? top - 10 : 0;
+      const int nbits = top - lo_bit + 1;
+      const uint64_t dmask = (1ull << nbits) - 1ull;
+      hist[threadIdx.x] = 0;
+      hist[threadIdx.x + NT] = 0;
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      if (first + i < P && (key[i] & mask) == prefix)
-        atomicAdd(&hist[(key[i] >> shift) & 0xff], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      // lane l holds digits 4l..4l+3; count of keys with a larger digit than each
-      const int l = threadIdx.x;
-      uint32_t c[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = hist[4 * l + j];
-      const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-      // suffix sum over lanes > l
-      uint32_t incl = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t w = __shfl_down(incl, o);
-        if (l + o < 64) incl += w;
+      for (int i = 0; i < KPT; ++i) {
+        if (first + i < P && (key[i] & mask) == prefix)
+          atomicAdd(&hist[(key[i] >> lo_bit) & dmask], 1u);
       }
-      uint32_t above = incl - mine;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < rem && rem <= above + c[j]) {
-          pick[0] = static_cast<uint32_t>(4 * l + j);
-          pick[1] = above;
-          pick[2] = c[j];
-        }
-        above += c[j];
-      }
+      __syncthreads();
+      uint32_t above, cnt;
+      const uint32_t digit = block_pick_bucket<NT, uint32_t>(
+          hist[2 * threadIdx.x], hist[2 * threadIdx.x + 1], rem, scan_lds, pick, &above, &cnt);
+      rem -= above;
+      prefix |= static_cast<uint64_t>(digit) << lo_bit;
+      mask |= dmask << lo_bit;
+      TWL_PHASE(7 + (npass < 4 ? npass : 4));
+      ++npass;
+      if (cnt == rem || lo_bit == 0) break;
+      top = lo_bit - 1;
     }
-    __syncthreads();
-    const uint32_t digit = pick[0], above = pick[1], cnt = pick[2];
-    __syncthreads();
-    rem -= above;
-    prefix |= static_cast<uint64_t>(digit) << shift;
-    mask |= 0xffull << shift;
-    if (cnt == rem) break;
   }
 
   // pages strictly above the boundary prefix are in; of the pages equal to it, the first
@@ -162,7 +189,7 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   for (int i = 0; i < KPT; ++i)
     n_eq += (first + i < P && (key[i] & mask) == prefix) ? 1u : 0u;
   uint32_t tot;
-  uint32_t eq_before = block_excl_scan_u32<1024>(n_eq, scan_lds, &tot);
+  uint32_t eq_before = block_excl_scan_u32<NT>(n_eq, scan_lds, &tot);
   bool chosen[KPT];
   uint32_t n_sel = 0;
 #pragma unroll
@@ -180,10 +207,12 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
     chosen[i] = c;
     n_sel += c ? 1u : 0u;
   }
-  uint32_t pos = block_excl_scan_u32<1024>(n_sel, scan_lds, &tot);
+  uint32_t pos = block_excl_scan_u32<NT>(n_sel, scan_lds, &tot);
+  TWL_PHASE(12);
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
     if (chosen[i]) out[pos++] = first + i;
+  TWL_PHASE(13);
 }
 
 template <int KPT>
@@ -202,7 +231,7 @@ size_t quest_workspace_bytes(const Layout& L) {
 
 hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
                                int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s) {
-  double* scores = static_cast<double*>(ws);
+  double* scores = static_cast<double*>(stage_scratch(ws, L));
   const dim3 grid((L.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, L.Hkv, L.B);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* mm = static_cast<const uint16_t*>(minmax);

@@ -16,45 +16,46 @@
 #include "twl_device.h"
 #include "twl_launch.h"
 
+TWL_PHASE_STORAGE(topp)
+
 namespace twl {
 namespace {
 
 constexpr int kToppThreads = 1024;
 constexpr int kBins = 2048;
 
-// Logical token of candidate slot `slot` of a unit, or -1 when it is not a valid candidate.
-__device__ __forceinline__ int slot_token(int slot, int n_slots, const int32_t* cand_row, int cnt,
-                                          int n, const int32_t* table_row, int num_phys) {
-  if (slot >= n_slots) return -1;
-  int t;
-  if (cand_row == nullptr) {
-    t = slot;
-  } else {
-    if (slot / kPage >= cnt) return -1;
-    const int pg = cand_row[slot / kPage];
-    if (pg < 0) return -1;
-    t = pg * kPage + slot % kPage;
-  }
-  if (t >= n || !phys_ok(table_row[t / kPage], num_phys)) return -1;
-  return t;
+// floor(W * 2^(40 - e)) for a non-negative fp32 W given by its bits, e the binary exponent
+// of the unit's largest W: integer shifts of the 24-bit significand (W < 2^(e+1), so the
+// result is below 2^41). Subnormal W (a tiny share of any sum) counts as 0.
+__device__ __forceinline__ uint64_t fixed_mass(uint32_t key, int e) {
+  const int ew = static_cast<int>(key >> 23) - 127;
+  if (ew < -126) return 0;
+  const uint64_t sig = (key & 0x7fffffu) | 0x800000u;
+  const int sh = ew - e + 17;  // W * 2^(40-e) = sig * 2^(ew - 23 + 40 - e)
+  if (sh >= 0) return sig << sh;
+  return sh <= -24 ? 0 : (sig >> (-sh));
 }
 
 // Each thread owns SPT consecutive slots. Up to 16 stay in registers for the whole search;
 // larger rows are processed as 16-slot tiles, with W staged once in the workspace (each
-// thread re-reads only what it wrote).
+// thread re-reads only what it wrote). A slot is a candidate when its page rank is below the
+// unit's candidate count and its token is inside the sequence; slots of unmapped pages
+// carry weight 0 from the estimate and are never kept (W > 0 is required).
 template <int SPT>
 __global__ __launch_bounds__(kToppThreads) void topp_kernel(
     const float* __restrict__ weights, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int Hkv,
-    int G, int max_pages, int num_phys, float p, int32_t* __restrict__ kept,
-    int32_t* __restrict__ kept_count, float* __restrict__ tau_out, float* __restrict__ stage) {
+    const int32_t* __restrict__ seq_lens, int Hkv, int G, int max_pages, float p,
+    int32_t* __restrict__ kept, int32_t* __restrict__ kept_count, float* __restrict__ tau_out,
+    float* __restrict__ stage) {
   constexpr int TILE = SPT < 16 ? SPT : 16;
   constexpr int NT = SPT / TILE;
+  constexpr int PG = (TILE + kPage - 1) / kPage;  // candidate pages a tile touches
   __shared__ unsigned long long mass[kBins];
   __shared__ uint32_t scan_u32[kToppThreads / kWave + 1];
   __shared__ uint64_t red64[kToppThreads / kWave];
-  __shared__ unsigned long long pick[2];
+  __shared__ uint64_t pick[3];
+  TWL_PHASE(0);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
   const long unit = static_cast<long>(b) * Hkv + g;
@@ -67,17 +68,40 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
     cnt = cand_count ? cand_count[unit] : (n + kPage - 1) / kPage;
     cnt = cnt < cand_stride_pages ? cnt : cand_stride_pages;
   }
-  const int32_t* table_row = page_table + static_cast<long>(b) * max_pages;
   const int first = threadIdx.x * SPT;
   float* my_stage = NT > 1 ? stage + unit * n_slots + first : nullptr;
   const float inv_g = 1.0f / static_cast<float>(G);  // exact: G is a power of two
 
-  // pass 0: W_j = mean of the group's weights on valid slots (0 elsewhere), range of W > 0
+  // logical token of the tile's slot i, or -1 (tile-local page ids preloaded in pg[])
+  auto token_of = [&](int f0, const int (&pg)[PG], int i) -> int {
+    const int slot = f0 + i;
+    if (slot >= n_slots) return -1;
+    int t;
+    if (cand_row == nullptr) {
+      t = slot;
+    } else {
+      const int pid = pg[(i + (f0 % kPage)) / kPage];
+      if (slot / kPage >= cnt || pid < 0) return -1;
+      t = pid * kPage + slot % kPage;
+    }
+    return t < n ? t : -1;
+  };
+  auto load_pages = [&](int f0, int (&pg)[PG]) {
+#pragma unroll
+    for (int j = 0; j < PG; ++j) {
+      const int r = f0 / kPage + j;
+      pg[j] = (cand_row != nullptr && r < cnt) ? cand_row[r] : -1;
+    }
+  };
+
+  // pass 0: W_j = mean of the group's weights on candidate slots (0 elsewhere)
   float W[TILE];
   uint32_t kmax = 0, kmin = 0xffffffffu;
 #pragma unroll 1
   for (int t = 0; t < NT; ++t) {
     const int f0 = first + t * TILE;
+    int pg[PG];
+    load_pages(f0, pg);
 #pragma unroll
     for (int i = 0; i < TILE; ++i) W[i] = 0.f;
     if (f0 < n_slots) {
@@ -102,8 +126,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
     }
 #pragma unroll
     for (int i = 0; i < TILE; ++i) {
-      const bool ok = slot_token(f0 + i, n_slots, cand_row, cnt, n, table_row, num_phys) >= 0;
-      W[i] = ok ? fmaxf(W[i] * inv_g, 0.f) : 0.f;
+      W[i] = token_of(f0, pg, i) >= 0 ? fmaxf(W[i] * inv_g, 0.f) : 0.f;
       const uint32_t k = __float_as_uint(W[i]);
       if (k > 0) {
         kmax = k > kmax ? k : kmax;
@@ -117,8 +140,10 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
             f32x4{W[i], W[i + 1], W[i + 2], W[i + 3]};
     }
   }
+  TWL_PHASE(1);
   kmax = block_max_u32<kToppThreads>(kmax, scan_u32);
   kmin = block_min_u32<kToppThreads>(kmin, scan_u32);
+  TWL_PHASE(2);
 
   // reload tile t of this thread's W (no-op when everything fits one tile)
   auto load_tile = [&](int t) {
@@ -145,23 +170,25 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
   } else if (kmax != 0) {
     // fixed-point masses relative to the largest weight's binade
     const int e = static_cast<int>((kmax >> 23) & 0xff) - 127;
-    const double fx = ldexp(1.0, 40 - e);
     uint64_t tsum = 0;
 #pragma unroll 1
     for (int t = 0; t < NT; ++t) {
       load_tile(t);
 #pragma unroll
-      for (int i = 0; i < TILE; ++i) tsum += static_cast<uint64_t>(static_cast<double>(W[i]) * fx);
+      for (int i = 0; i < TILE; ++i) tsum += fixed_mass(__float_as_uint(W[i]), e);
     }
     const uint64_t T = block_sum_u64<kToppThreads>(tsum, red64);
+    TWL_PHASE(3);
     uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(p) * static_cast<double>(T)));
     rem = rem < 1 ? 1 : rem;
     uint32_t lo = kmin, hi = kmax;
+    int pass_no = 0;
     for (;;) {
       const uint32_t range = hi - lo;
       const int bits = range == 0 ? 0 : 32 - __clz(range);
       const int shift = bits > 11 ? bits - 11 : 0;
-      for (int i = threadIdx.x; i < kBins; i += kToppThreads) mass[i] = 0ull;
+      mass[threadIdx.x] = 0ull;
+      mass[threadIdx.x + kToppThreads] = 0ull;
       __syncthreads();
 #pragma unroll 1
       for (int t = 0; t < NT; ++t) {
@@ -169,50 +196,30 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
 #pragma unroll
         for (int i = 0; i < TILE; ++i) {
           const uint32_t k = __float_as_uint(W[i]);
-          const uint64_t m = static_cast<uint64_t>(static_cast<double>(W[i]) * fx);
-          if (m != 0 && k >= lo && k <= hi) atomicAdd(&mass[(k - lo) >> shift], m);
+          if (k >= lo && k <= hi) {
+            const uint64_t m = fixed_mass(k, e);
+            if (m != 0) atomicAdd(&mass[(k - lo) >> shift], m);
+          }
         }
       }
       __syncthreads();
-      // bucket b* with mass(buckets > b*) < rem <= mass(buckets >= b*); thread t holds
-      // buckets 2t and 2t+1
-      {
-        const int t = threadIdx.x;
-        const uint64_t m0 = mass[2 * t], m1 = mass[2 * t + 1];
-        const int w = t / kWave;
-        const uint64_t incl = wave_incl_scan_u64(m0 + m1);
-        if (lane_id() == kWave - 1) red64[w] = incl;
-        __syncthreads();
-        uint64_t before = 0, total = 0;
-        for (int i = 0; i < kToppThreads / kWave; ++i) {
-          const uint64_t v = red64[i];
-          if (i < w) before += v;
-          total += v;
-        }
-        const uint64_t above1 = total - (before + incl);  // buckets > 2t+1
-        const uint64_t above0 = above1 + m1;              // buckets > 2t
-        if (above1 < rem && rem <= above1 + m1) {
-          pick[0] = 2 * t + 1;
-          pick[1] = above1;
-        } else if (above0 < rem && rem <= above0 + m0) {
-          pick[0] = 2 * t;
-          pick[1] = above0;
-        }
-        __syncthreads();
-      }
-      const uint32_t bucket = static_cast<uint32_t>(pick[0]);
-      rem -= pick[1];
-      __syncthreads();
+      uint64_t above, inb;
+      const uint32_t bucket = block_pick_bucket<kToppThreads, uint64_t>(
+          mass[2 * threadIdx.x], mass[2 * threadIdx.x + 1], rem, red64, pick, &above, &inb);
+      rem -= above;
       const uint32_t nlo = lo + (bucket << shift);
       const uint32_t span = (1u << shift) - 1u;
       const uint32_t nhi = (hi - nlo) < span ? hi : nlo + span;
       lo = nlo;
       hi = nhi;
+      TWL_PHASE(4 + (pass_no < 4 ? pass_no : 4));
+      ++pass_no;
       if (shift == 0) break;
     }
     tau = __uint_as_float(lo);
   }
 
+  TWL_PHASE(9);
   // compaction in slot order
   uint32_t nk = 0;
 #pragma unroll 1
@@ -223,21 +230,24 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
   }
   uint32_t total;
   uint32_t pos = block_excl_scan_u32<kToppThreads>(nk, scan_u32, &total);
+  TWL_PHASE(10);
   int32_t* out = kept + unit * n_slots;
 #pragma unroll 1
   for (int t = 0; t < NT; ++t) {
+    const int f0 = first + t * TILE;
+    int pg[PG];
+    load_pages(f0, pg);
     load_tile(t);
 #pragma unroll
     for (int i = 0; i < TILE; ++i) {
-      if (W[i] > 0.f && W[i] >= tau)
-        out[pos++] = slot_token(first + t * TILE + i, n_slots, cand_row, cnt, n, table_row,
-                                num_phys);
+      if (W[i] > 0.f && W[i] >= tau) out[pos++] = token_of(f0, pg, i);
     }
   }
   if (threadIdx.x == 0) {
     kept_count[unit] = static_cast<int32_t>(total);
     if (tau_out) tau_out[unit] = tau;
   }
+  TWL_PHASE(11);
 }
 
 template <int SPT>
@@ -245,8 +255,8 @@ void topp_launch(const Layout& L, const float* weights, const int32_t* cand_page
                  const int32_t* cand_count, int stride, float p, int32_t* kept,
                  int32_t* kept_count, float* tau, float* stage, hipStream_t s) {
   topp_kernel<SPT><<<dim3(L.Hkv, L.B), kToppThreads, 0, s>>>(
-      weights, cand_pages, cand_count, stride, L.seq_lens, L.page_table, L.Hkv, L.G(),
-      L.max_pages, L.num_phys, p, kept, kept_count, tau, stage);
+      weights, cand_pages, cand_count, stride, L.seq_lens, L.Hkv, L.G(), L.max_pages, p, kept,
+      kept_count, tau, stage);
 }
 
 }  // namespace
@@ -263,7 +273,7 @@ hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* can
                        hipStream_t s) {
   const int n_slots = cand_stride_pages * kPage;
   const int spt = (n_slots + kToppThreads - 1) / kToppThreads;
-  float* st = static_cast<float*>(ws);
+  float* st = static_cast<float*>(stage_scratch(ws, L));
   if (spt <= 1) topp_launch<1>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
   else if (spt <= 2) topp_launch<2>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
   else if (spt <= 4) topp_launch<4>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);

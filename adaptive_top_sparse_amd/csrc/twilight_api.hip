@@ -176,7 +176,8 @@ int twilight_topp_select(const twl_layout_t* L, const float* weights, const int3
     return TWL_ERR_UNSUPPORTED;
   if (empty) return TWL_OK;
   const size_t need = twl::topp_workspace_bytes(lay, cand_stride_pages);
-  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) ||
+                   workspace_bytes < need))
     return TWL_ERR_WORKSPACE;
   return launch_status(twl::launch_topp(lay, weights, cand_pages, cand_count, cand_stride_pages,
                                         p, kept, kept_count, tau, workspace, stream));

@@ -6,6 +6,54 @@
 
 #include "twl_launch.h"
 
+// Opt-in phase timing for tuning builds (-DTWL_PHASE_TIMING): work-group 0 / thread 0 of a
+// kernel stores the 100 MHz real-time clock at marked phase boundaries in a per-file device array that
+// an exported twl_phase_<file>() copies out. Compiled out otherwise.
+#ifdef TWL_PHASE_TIMING
+#define TWL_PHASE_STORAGE(NAME)                                                       \
+  static __device__ unsigned long long twl_phase_ts[32];                              \
+  extern "C" void twl_phase_##NAME(unsigned long long* host) {                        \
+    (void)hipMemcpyFromSymbol(host, HIP_SYMBOL(twl_phase_ts), sizeof(twl_phase_ts));  \
+  }
+#define TWL_PHASE(i)                                                                   \
+  do {                                                                                 \
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)     \
+      twl_phase_ts[i] = __builtin_amdgcn_s_memrealtime();                                  \
+  } while (0)
+// start and end clock of every work-group (linear id < 32768) and the XCC it ran on
+#define TWL_SPAN_STORAGE(NAME)                                                         \
+  static __device__ unsigned long long twl_span_ts[3 * 32768];                         \
+  extern "C" void twl_span_##NAME(unsigned long long* host) {                          \
+    (void)hipMemcpyFromSymbol(host, HIP_SYMBOL(twl_span_ts), sizeof(twl_span_ts));     \
+  }
+#define TWL_BLOCK_LINEAR() \
+  ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x)
+#define TWL_SPAN_BEGIN()                                                               \
+  do {                                                                                 \
+    if (threadIdx.x == 0 && TWL_BLOCK_LINEAR() < 32768) {                              \
+      twl_span_ts[3 * TWL_BLOCK_LINEAR()] = __builtin_amdgcn_s_memrealtime();          \
+      twl_span_ts[3 * TWL_BLOCK_LINEAR() + 2] = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)); \
+    }                                                                                  \
+  } while (0)
+#define TWL_SPAN_END()                                                                 \
+  do {                                                                                 \
+    if (threadIdx.x == 0 && TWL_BLOCK_LINEAR() < 32768)                                \
+      twl_span_ts[3 * TWL_BLOCK_LINEAR() + 1] = __builtin_amdgcn_s_memrealtime();      \
+  } while (0)
+#else
+#define TWL_SPAN_STORAGE(NAME)
+#define TWL_SPAN_BEGIN() \
+  do {                   \
+  } while (0)
+#define TWL_SPAN_END() \
+  do {                 \
+  } while (0)
+#define TWL_PHASE_STORAGE(NAME)
+#define TWL_PHASE(i) \
+  do {               \
+  } while (0)
+#endif
+
 namespace twl {
 
 constexpr int kWave = 64;
@@ -33,156 +81,238 @@ __device__ __forceinline__ bool phys_ok(int phys, int num_phys) {
   return phys >= 0 && phys < num_phys;
 }
 
-// ---- wave reductions (64 lanes) -------------------------------------------------------
+// ---- cross-lane moves ------------------------------------------------------------------
+// DPP controls (GFX9 encoding).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowShr1 = 0x111;
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// DPP move; lanes without a source (or outside row_mask) read 0.
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, RM, 0xF, true));
+}
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL, RM>(__builtin_bit_cast(uint32_t, v)));
+}
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, RM>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_u32<CTRL, RM>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <typename T>
+__device__ __forceinline__ T readlane(T v, int lane) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u), lane);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+    return __builtin_bit_cast(T, (static_cast<uint64_t>(hi) << 32) | lo);
+  } else {
+    return __builtin_bit_cast(
+        T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+  }
+}
+
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_any(T v) {
+  if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, dpp_u64<CTRL>(__builtin_bit_cast(uint64_t, v)));
+  } else {
+    return __builtin_bit_cast(T, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+  }
+}
+
+struct OpSum {
+  template <typename T> __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+  template <typename T> __device__ T operator()(T a, T b) const { return a > b ? a : b; }
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMin {
+  template <typename T> __device__ T operator()(T a, T b) const { return a < b ? a : b; }
+};
+
+// Reduction over the whole wave, result uniform: DPP inside each 16-lane row (every lane of
+// a row ends with the row result, each step combining a commutative pair), then the four
+// rows combined through readlane in a fixed order. Every lane must be active.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp_any<kQuadXor1>(v));
+  v = op(v, dpp_any<kQuadXor2>(v));
+  v = op(v, dpp_any<kRowHalfMirror>(v));
+  v = op(v, dpp_any<kRowMirror>(v));
+  return op(op(readlane(v, 0), readlane(v, 16)), op(readlane(v, 32), readlane(v, 48)));
+}
+
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax()); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpSum()); }
+
+// Sum over aligned groups of W lanes (W in {2, 4, 8, 16}) with DPP; every lane of a group
+// ends with the bit-identical total.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group width");
+  v += dpp_f32<kQuadXor1>(v);
+  if constexpr (W >= 4) v += dpp_f32<kQuadXor2>(v);
+  if constexpr (W >= 8) v += dpp_f32<kRowHalfMirror>(v);
+  if constexpr (W >= 16) v += dpp_f32<kRowMirror>(v);
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t w = __shfl_xor(v, o);
-    v = w > v ? w : v;
+// Combine the lanes that hold the same position within their W-lane group, over all
+// 64 / W groups of the wave (W in {8, 16}); every lane ends with the combined value. Uses
+// a DPP rotate inside rows and the gfx950 permlane swaps across rows.
+template <int W, typename Op>
+__device__ __forceinline__ float across_groups(float v, Op op) {
+  static_assert(W == 8 || W == 16, "group width");
+  if constexpr (W == 8) v = op(v, dpp_f32<kRowRor8>(v));
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v),
+                                                    __builtin_bit_cast(int, v), false, false);
+    v = op(__builtin_bit_cast(float, static_cast<int>(r[0])),
+           __builtin_bit_cast(float, static_cast<int>(r[1])));
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v),
+                                                    __builtin_bit_cast(int, v), false, false);
+    v = op(__builtin_bit_cast(float, static_cast<int>(r[0])),
+           __builtin_bit_cast(float, static_cast<int>(r[1])));
   }
   return v;
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t w = __shfl_xor(v, o);
-    v = w < v ? w : v;
+// Inclusive prefix sum over the 64 lanes: row-local Hillis-Steele shifts, then the row
+// totals carried across rows with row_bcast.
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T x) {
+  x += dpp_any<kRowShr1>(x);
+  x += dpp_any<kRowShr2>(x);
+  x += dpp_any<kRowShr4>(x);
+  x += dpp_any<kRowShr8>(x);
+  if constexpr (sizeof(T) == 8) {
+    x += __builtin_bit_cast(T, dpp_u64<kRowBcast15, 0xA>(__builtin_bit_cast(uint64_t, x)));
+    x += __builtin_bit_cast(T, dpp_u64<kRowBcast31, 0xC>(__builtin_bit_cast(uint64_t, x)));
+  } else {
+    x += __builtin_bit_cast(T, dpp_u32<kRowBcast15, 0xA>(__builtin_bit_cast(uint32_t, x)));
+    x += __builtin_bit_cast(T, dpp_u32<kRowBcast31, 0xC>(__builtin_bit_cast(uint32_t, x)));
   }
-  return v;
+  return x;
 }
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+// ---- block-wide primitives (blockDim.x == NT, a multiple of 64, at most 1024) ----------
+// Each takes an LDS scratch of NT/64 elements and ends with a barrier, so the scratch may
+// be reused by the next call.
 
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t w = __shfl_up(v, o);
-    if (l >= o) v += w;
-  }
-  return v;
-}
-
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t w = __shfl_up(v, o);
-    if (l >= o) v += w;
-  }
-  return v;
-}
-
-// ---- block-wide primitives (blockDim.x == NT, a multiple of 64) -----------------------
-
-// Exclusive prefix sum of one value per thread, in thread order. `lds` holds NT/64 + 1
-// words. Returns the exclusive prefix; *total receives the block total.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* lds,
-                                                        uint32_t* total) {
+template <int NT, typename T, typename Op>
+__device__ __forceinline__ T block_reduce(T v, T* lds, Op op, T identity) {
   constexpr int NW = NT / kWave;
-  const int w = threadIdx.x / kWave;
-  const uint32_t incl = wave_incl_scan_u32(v);
-  if (lane_id() == kWave - 1) lds[w] = incl;
+  v = wave_reduce(v, op);
+  if (lane_id() == 0) lds[threadIdx.x / kWave] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < NW; ++i) {
-      const uint32_t t = lds[i];
-      lds[i] = run;
-      run += t;
-    }
-    lds[NW] = run;
-  }
+  T x = lane_id() < NW ? lds[lane_id()] : identity;
+  x = wave_reduce(x, op);
   __syncthreads();
-  const uint32_t res = lds[w] + incl - v;
-  *total = lds[NW];
-  __syncthreads();
-  return res;
+  return x;
 }
 
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* lds) {
-  constexpr int NW = NT / kWave;
-  v = wave_max(v);
-  if (lane_id() == 0) lds[threadIdx.x / kWave] = v;
-  __syncthreads();
-  float r = lds[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) r = fmaxf(r, lds[i]);
-  __syncthreads();
-  return r;
+  return block_reduce<NT>(v, lds, OpMax(), -INFINITY);
 }
-
 template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* lds) {
-  constexpr int NW = NT / kWave;
-  v = wave_sum(v);
-  if (lane_id() == 0) lds[threadIdx.x / kWave] = v;
-  __syncthreads();
-  float r = 0.f;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) r += lds[i];
-  __syncthreads();
-  return r;
+  return block_reduce<NT>(v, lds, OpSum(), 0.f);
 }
-
 template <int NT>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* lds) {
-  constexpr int NW = NT / kWave;
-  v = wave_max_u32(v);
-  if (lane_id() == 0) lds[threadIdx.x / kWave] = v;
-  __syncthreads();
-  uint32_t r = lds[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) r = lds[i] > r ? lds[i] : r;
-  __syncthreads();
-  return r;
+  return block_reduce<NT>(v, lds, OpMax(), 0u);
 }
-
 template <int NT>
 __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, uint32_t* lds) {
+  return block_reduce<NT>(v, lds, OpMin(), 0xffffffffu);
+}
+template <int NT>
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* lds) {
+  return block_reduce<NT>(v, lds, OpSum(), uint64_t(0));
+}
+template <int NT>
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* lds) {
+  return block_reduce<NT>(v, lds, OpMax(), uint64_t(0));
+}
+template <int NT>
+__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* lds) {
+  return block_reduce<NT>(v, lds, OpMin(), ~uint64_t(0));
+}
+
+// Exclusive prefix sum of one value per thread, in thread order; *total gets the sum.
+template <int NT, typename T>
+__device__ __forceinline__ T block_excl_scan(T v, T* lds, T* total) {
   constexpr int NW = NT / kWave;
-  v = wave_min_u32(v);
-  if (lane_id() == 0) lds[threadIdx.x / kWave] = v;
+  const int w = threadIdx.x / kWave;
+  const T incl = wave_incl_scan(v);
+  if (lane_id() == kWave - 1) lds[w] = incl;
   __syncthreads();
-  uint32_t r = lds[0];
-#pragma unroll
-  for (int i = 1; i < NW; ++i) r = lds[i] < r ? lds[i] : r;
+  T x = lane_id() < NW ? lds[lane_id()] : T(0);
+  x = wave_incl_scan(x);
+  const T before = w > 0 ? readlane(x, w - 1) : T(0);
+  *total = readlane(x, NW - 1);
   __syncthreads();
-  return r;
+  return before + incl - v;
 }
 
 template <int NT>
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* lds) {
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* lds,
+                                                        uint32_t* total) {
+  return block_excl_scan<NT, uint32_t>(v, lds, total);
+}
+
+// Boundary bucket of a descending selection over 2 * NT buckets, thread t holding buckets
+// 2t and 2t+1 with weights w0, w1: the bucket b* with weight(buckets > b*) < rem <=
+// weight(buckets >= b*). Returns b*; *above = weight(buckets > b*), *in = weight(b*).
+// `lds` holds NT/64 elements, `pick` 3. Requires 0 < rem <= total weight.
+template <int NT, typename T>
+__device__ __forceinline__ uint32_t block_pick_bucket(T w0, T w1, T rem, T* lds, T* pick,
+                                                      T* above, T* in) {
   constexpr int NW = NT / kWave;
-  v = wave_sum_u64(v);
-  if (lane_id() == 0) lds[threadIdx.x / kWave] = v;
+  const int t = threadIdx.x;
+  const int w = t / kWave;
+  const T incl = wave_incl_scan(static_cast<T>(w0 + w1));
+  if (lane_id() == kWave - 1) lds[w] = incl;
   __syncthreads();
-  uint64_t r = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) r += lds[i];
+  T x = lane_id() < NW ? lds[lane_id()] : T(0);
+  x = wave_incl_scan(x);
+  const T before = w > 0 ? readlane(x, w - 1) : T(0);
+  const T total = readlane(x, NW - 1);
+  const T above1 = total - (before + incl);  // buckets > 2t+1
+  const T above0 = above1 + w1;              // buckets > 2t
+  if (above1 < rem && rem <= above1 + w1) {
+    pick[0] = static_cast<T>(2 * t + 1);
+    pick[1] = above1;
+    pick[2] = w1;
+  } else if (above0 < rem && rem <= above0 + w0) {
+    pick[0] = static_cast<T>(2 * t);
+    pick[1] = above0;
+    pick[2] = w0;
+  }
   __syncthreads();
-  return r;
+  const uint32_t b = static_cast<uint32_t>(pick[0]);
+  *above = pick[1];
+  *in = pick[2];
+  __syncthreads();
+  return b;
 }
 
 // ---- number formats -------------------------------------------------------------------

@@ -8,6 +8,8 @@
 
 namespace twl {
 
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
 // Tokens per KV-cache page.
 constexpr int kPage = 16;
 
@@ -48,11 +50,14 @@ hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_ca
                                 const int32_t* kept_count, int kept_stride, float sm_scale,
                                 void* out, void* ws, hipStream_t s);
 
+// Every call uses the workspace as scratch for its own duration only; nothing in it needs
+// to survive between calls or be initialised by the caller.
+inline void* stage_scratch(void* ws, const Layout&) { return ws; }
+
 // Largest slot count per unit the top-p kernel holds on chip.
 constexpr int kToppMaxSlots = 65536;
 // Largest page count per sequence the Quest selector holds on chip.
 constexpr int kQuestMaxPages = 32768;
 
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace twl
