@@ -337,6 +337,16 @@ def test_topp_special_cases():
     assert list(kept) == [int(np.argmax(W))]
 
 
+def test_topp_mass_exactly_at_target_stops_there():
+    # mass reaches p * total exactly after two tokens (all values exact in binary): the
+    # nucleus is those two, the lower slot winning the tie between the 0.25s
+    W = np.array([0.5, 0.25, 0.25])
+    kept, tau = oracle.topp_select(W[None], np.ones(3, bool), 0.75)
+    assert list(kept) == [0, 1] and tau == 0.25
+    m_star, _ = _brute_force_min_nucleus(list(W), 0.75)
+    assert m_star == 2
+
+
 def test_topp_one_hot_at_p_one_keeps_only_positive_weights():
     onehot = np.zeros(30)
     onehot[17] = 1.0
