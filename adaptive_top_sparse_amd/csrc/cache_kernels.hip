@@ -80,7 +80,9 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
 }
 
 // One wave per (sequence, logical page, KV head); each lane owns D/64 channels and walks
-// the page's valid tokens in order, so the first occurrence of a tied min/max is kept.
+// the page's valid tokens in order, so the first occurrence of a tied min/max is kept. The
+// bounds go to the page's logical slot [b, kvh, page], so that one KV head's bounds form a
+// contiguous stretch for the scorer.
 template <int D>
 __global__ __launch_bounds__(256) void page_bounds_kernel(
     const uint16_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
@@ -124,7 +126,8 @@ __global__ __launch_bounds__(256) void page_bounds_kernel(
       }
     }
   }
-  uint16_t* dst = minmax + blk * 2 * D + lane_id() * CPL;
+  uint16_t* dst =
+      minmax + ((static_cast<long>(b) * Hkv + kvh) * max_pages + page) * 2 * D + lane_id() * CPL;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     dst[c] = lo[c];

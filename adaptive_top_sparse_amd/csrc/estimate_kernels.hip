@@ -30,7 +30,6 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   constexpr int Hq_per = G;
   __shared__ float qs[G][D];
   __shared__ float qsum[G][NG];
-  __shared__ float red[kEstChunk / kWave];
   TWL_PHASE(0);
   const int b = blockIdx.z;
   const int g = blockIdx.y;

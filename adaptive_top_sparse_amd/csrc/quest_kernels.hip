@@ -14,47 +14,57 @@
 #include "twl_launch.h"
 
 TWL_PHASE_STORAGE(quest)
+TWL_SPAN_STORAGE(quest)
 
 namespace twl {
 namespace {
 
-constexpr int kScorePagesPerBlock = 64;
+#ifndef TWL_SCORE_THREADS
+#define TWL_SCORE_THREADS 256
+#endif
+#ifndef TWL_SCORE_ROUNDS
+#define TWL_SCORE_ROUNDS 4
+#endif
+constexpr int kScoreThreads = TWL_SCORE_THREADS;
+constexpr int kScoreRounds = TWL_SCORE_ROUNDS;
 
-// Lanes per page = D/8 (each lane owns 8 channels = 16 B of lo and 16 B of hi). A block of
-// 256 threads covers 256/LPP pages per round and all rounds' page ids and bounds are
-// loaded before any arithmetic, so each lane has 2 * ROUNDS loads in flight.
+// Lanes per page = D/8 (each lane owns 8 channels = 16 B of lo and 16 B of hi). A block
+// covers kScoreThreads/LPP consecutive logical pages per round, kScoreRounds rounds, read
+// as one contiguous stretch of the KV head's bounds; all rounds' loads are issued before
+// any arithmetic, so each lane has 2 * rounds loads in flight.
 template <int D>
-__global__ __launch_bounds__(256) void quest_score_kernel(
+constexpr int score_pages_per_block() {
+  return kScoreThreads / (D / 8) * kScoreRounds;
+}
+
+template <int D>
+__global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ minmax,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int Hq,
-    int Hkv, int max_pages, int num_phys, double* __restrict__ scores) {
+    const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int max_pages,
+    double* __restrict__ scores) {
   constexpr int LPP = D / 8;
-  constexpr int PPI = 256 / LPP;  // pages per round
-  constexpr int ROUNDS = kScorePagesPerBlock / PPI;
+  constexpr int PPI = kScoreThreads / LPP;  // pages per round
+  constexpr int ROUNDS = kScoreRounds;
+  constexpr int PPB = PPI * ROUNDS;
   TWL_PHASE(0);
+  TWL_SPAN_BEGIN();
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int G = Hq / Hkv;
   const int n = seq_len_clamped(seq_lens, b, max_pages);
   const int P = (n + kPage - 1) / kPage;
-  const int p0 = blockIdx.x * kScorePagesPerBlock;
+  const int p0 = blockIdx.x * PPB;
   if (p0 >= P) return;
   const int sub = threadIdx.x % LPP;
   const int c0 = sub * 8;
-  const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
-
-  int phys[ROUNDS];
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    const int p = p0 + r * PPI + threadIdx.x / LPP;
-    phys[r] = p < P ? trow[p] : -1;
-    if (!phys_ok(phys[r], num_phys)) phys[r] = -1;
-  }
+  // this KV head's bounds, in logical page order
+  const uint16_t* unit_mm = minmax + (static_cast<long>(b) * Hkv + g) * max_pages * 2 * D;
   u32x4 lo[ROUNDS], hi[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    if (phys[r] >= 0) {
-      const uint16_t* blk = minmax + (static_cast<long>(phys[r]) * Hkv + g) * 2 * D + c0;
+    const int p = p0 + r * PPI + threadIdx.x / LPP;
+    if (p < P) {
+      const uint16_t* blk = unit_mm + static_cast<long>(p) * 2 * D + c0;
       lo[r] = *reinterpret_cast<const u32x4*>(blk);
       hi[r] = *reinterpret_cast<const u32x4*>(blk + D);
     } else {
@@ -97,6 +107,7 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
     if (sub == 0 && p < P) out[p] = acc;
   }
   TWL_PHASE(2);
+  TWL_SPAN_END();
 }
 
 // One 1024-thread block per (sequence, KV head); thread t owns pages [t*KPT, t*KPT+KPT).
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   constexpr int kBins = 2 * NT;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t scan_lds[NT / kWave + 1];
-  __shared__ uint64_t red64[NT / kWave];
+  __shared__ uint64_t red64[NT / kWave], red64b[NT / kWave];
   __shared__ uint32_t pick[3];
   TWL_PHASE(4);
   const int b = blockIdx.y;
@@ -141,13 +152,13 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
     }
   }
   TWL_PHASE(5);
-  kmin = block_min_u64<NT>(kmin, red64);
-  kmax = block_max_u64<NT>(kmax, red64);
+  block_minmax<NT, uint64_t>(kmin, kmax, red64, red64b, ~0ull, 0ull, &kmin, &kmax);
   TWL_PHASE(6);
 
   // bits above `top` are common to every key
   uint64_t prefix, mask;
   uint32_t rem = static_cast<uint32_t>(m);
+  bool all_eq_in = false;  // every key equal to the final prefix is selected
   if (kmin == kmax) {
     prefix = kmax;
     mask = ~0ull;
@@ -177,19 +188,23 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
       mask |= dmask << lo_bit;
       TWL_PHASE(7 + (npass < 4 ? npass : 4));
       ++npass;
+      if (cnt == rem) all_eq_in = true;
       if (cnt == rem || lo_bit == 0) break;
       top = lo_bit - 1;
     }
   }
 
   // pages strictly above the boundary prefix are in; of the pages equal to it, the first
-  // `rem` in page order are in
-  uint32_t n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i)
-    n_eq += (first + i < P && (key[i] & mask) == prefix) ? 1u : 0u;
+  // `rem` in page order are in (all of them unless exact ties remain)
   uint32_t tot;
-  uint32_t eq_before = block_excl_scan_u32<NT>(n_eq, scan_lds, &tot);
+  uint32_t eq_before = 0;
+  if (!all_eq_in) {
+    uint32_t n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      n_eq += (first + i < P && (key[i] & mask) == prefix) ? 1u : 0u;
+    eq_before = block_excl_scan_u32<NT>(n_eq, scan_lds, &tot);
+  }
   bool chosen[KPT];
   uint32_t n_sel = 0;
 #pragma unroll
@@ -200,7 +215,7 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
       if (km > prefix) {
         c = true;
       } else if (km == prefix) {
-        c = eq_before < rem;
+        c = all_eq_in || eq_before < rem;
         ++eq_before;
       }
     }
@@ -232,15 +247,18 @@ size_t quest_workspace_bytes(const Layout& L) {
 hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
                                int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s) {
   double* scores = static_cast<double*>(stage_scratch(ws, L));
-  const dim3 grid((L.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, L.Hkv, L.B);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* mm = static_cast<const uint16_t*>(minmax);
   if (L.d == 128) {
-    quest_score_kernel<128><<<grid, 256, 0, s>>>(qq, mm, L.page_table, L.seq_lens, L.Hq, L.Hkv,
-                                                 L.max_pages, L.num_phys, scores);
+    constexpr int ppb = score_pages_per_block<128>();
+    const dim3 grid((L.max_pages + ppb - 1) / ppb, L.Hkv, L.B);
+    quest_score_kernel<128><<<grid, kScoreThreads, 0, s>>>(qq, mm, L.seq_lens, L.Hq, L.Hkv,
+                                                           L.max_pages, scores);
   } else {
-    quest_score_kernel<64><<<grid, 256, 0, s>>>(qq, mm, L.page_table, L.seq_lens, L.Hq, L.Hkv,
-                                                L.max_pages, L.num_phys, scores);
+    constexpr int ppb = score_pages_per_block<64>();
+    const dim3 grid((L.max_pages + ppb - 1) / ppb, L.Hkv, L.B);
+    quest_score_kernel<64><<<grid, kScoreThreads, 0, s>>>(qq, mm, L.seq_lens, L.Hq, L.Hkv,
+                                                          L.max_pages, scores);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
   constexpr int NT = SPT / TILE;
   constexpr int PG = (TILE + kPage - 1) / kPage;  // candidate pages a tile touches
   __shared__ unsigned long long mass[kBins];
-  __shared__ uint32_t scan_u32[kToppThreads / kWave + 1];
+  __shared__ uint32_t scan_u32[kToppThreads / kWave + 1], scan_u32b[kToppThreads / kWave];
   __shared__ uint64_t red64[kToppThreads / kWave];
   __shared__ uint64_t pick[3];
   TWL_PHASE(0);
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
     }
   }
   TWL_PHASE(1);
-  kmax = block_max_u32<kToppThreads>(kmax, scan_u32);
-  kmin = block_min_u32<kToppThreads>(kmin, scan_u32);
+  block_minmax<kToppThreads, uint32_t>(kmin, kmax, scan_u32, scan_u32b, 0xffffffffu, 0u, &kmin,
+                                       &kmax);
   TWL_PHASE(2);
 
   // reload tile t of this thread's W (no-op when everything fits one tile)
@@ -170,17 +170,10 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
   } else if (kmax != 0) {
     // fixed-point masses relative to the largest weight's binade
     const int e = static_cast<int>((kmax >> 23) & 0xff) - 127;
-    uint64_t tsum = 0;
-#pragma unroll 1
-    for (int t = 0; t < NT; ++t) {
-      load_tile(t);
-#pragma unroll
-      for (int i = 0; i < TILE; ++i) tsum += fixed_mass(__float_as_uint(W[i]), e);
-    }
-    const uint64_t T = block_sum_u64<kToppThreads>(tsum, red64);
     TWL_PHASE(3);
-    uint64_t rem = static_cast<uint64_t>(ceil(static_cast<double>(p) * static_cast<double>(T)));
-    rem = rem < 1 ? 1 : rem;
+    // the first pass covers every positive W, so its scan yields the total mass and the
+    // target ceil(p * total)
+    uint64_t rem = 0;
     uint32_t lo = kmin, hi = kmax;
     int pass_no = 0;
     for (;;) {
@@ -205,7 +198,8 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
       __syncthreads();
       uint64_t above, inb;
       const uint32_t bucket = block_pick_bucket<kToppThreads, uint64_t>(
-          mass[2 * threadIdx.x], mass[2 * threadIdx.x + 1], rem, red64, pick, &above, &inb);
+          mass[2 * threadIdx.x], mass[2 * threadIdx.x + 1], rem, red64, pick, &above, &inb,
+          pass_no == 0 ? p : 0.f, &rem);
       rem -= above;
       const uint32_t nlo = lo + (bucket << shift);
       const uint32_t span = (1u << shift) - 1u;

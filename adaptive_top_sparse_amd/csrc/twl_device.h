@@ -257,6 +257,25 @@ __device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t* lds) {
   return block_reduce<NT>(v, lds, OpMin(), ~uint64_t(0));
 }
 
+// Minimum and maximum of one value per thread in a single exchange.
+template <int NT, typename T>
+__device__ __forceinline__ void block_minmax(T vmin, T vmax, T* lds_min, T* lds_max, T id_min,
+                                             T id_max, T* out_min, T* out_max) {
+  constexpr int NW = NT / kWave;
+  vmin = wave_reduce(vmin, OpMin());
+  vmax = wave_reduce(vmax, OpMax());
+  if (lane_id() == 0) {
+    lds_min[threadIdx.x / kWave] = vmin;
+    lds_max[threadIdx.x / kWave] = vmax;
+  }
+  __syncthreads();
+  T a = lane_id() < NW ? lds_min[lane_id()] : id_min;
+  T b = lane_id() < NW ? lds_max[lane_id()] : id_max;
+  *out_min = wave_reduce(a, OpMin());
+  *out_max = wave_reduce(b, OpMax());
+  __syncthreads();
+}
+
 // Exclusive prefix sum of one value per thread, in thread order; *total gets the sum.
 template <int NT, typename T>
 __device__ __forceinline__ T block_excl_scan(T v, T* lds, T* total) {
@@ -283,9 +302,12 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* ld
 // 2t and 2t+1 with weights w0, w1: the bucket b* with weight(buckets > b*) < rem <=
 // weight(buckets >= b*). Returns b*; *above = weight(buckets > b*), *in = weight(b*).
 // `lds` holds NT/64 elements, `pick` 3. Requires 0 < rem <= total weight.
+// When frac > 0, rem is replaced by max(1, ceil(frac * total weight)) and *rem_used
+// receives it, so a first pass needs no separate reduction for the total.
 template <int NT, typename T>
 __device__ __forceinline__ uint32_t block_pick_bucket(T w0, T w1, T rem, T* lds, T* pick,
-                                                      T* above, T* in) {
+                                                      T* above, T* in, float frac = 0.f,
+                                                      T* rem_used = nullptr) {
   constexpr int NW = NT / kWave;
   const int t = threadIdx.x;
   const int w = t / kWave;
@@ -296,6 +318,11 @@ __device__ __forceinline__ uint32_t block_pick_bucket(T w0, T w1, T rem, T* lds,
   x = wave_incl_scan(x);
   const T before = w > 0 ? readlane(x, w - 1) : T(0);
   const T total = readlane(x, NW - 1);
+  if (frac > 0.f) {
+    rem = static_cast<T>(ceil(static_cast<double>(frac) * static_cast<double>(total)));
+    rem = rem < T(1) ? T(1) : rem;
+    if (rem_used) *rem_used = rem;
+  }
   const T above1 = total - (before + incl);  // buckets > 2t+1
   const T above0 = above1 + w1;              // buckets > 2t
   if (above1 < rem && rem <= above1 + w1) {

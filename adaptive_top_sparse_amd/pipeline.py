@@ -89,8 +89,8 @@ def upload(w, device="cuda", with_bounds: Optional[bool] = None) -> DeviceCache:
         k_cache=k_paged, v_cache=v_paged,
         k_codes=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 2), dtype=torch.uint8, device=dev),
         k_meta=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 32, 2), dtype=torch.float16, device=dev),
-        page_minmax=(torch.zeros((P, s.Hkv, 2, s.d), dtype=torch.float16, device=dev)
-                     if with_bounds else None))
+        page_minmax=(torch.zeros((s.B, s.Hkv, w.max_pages, 2, s.d), dtype=torch.float16,
+                                 device=dev) if with_bounds else None))
 
 
 @dataclasses.dataclass

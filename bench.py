@@ -40,7 +40,52 @@ def parse():
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for scaling HBM "
+                         "traffic counters) and exit")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, five times: HBM counters read on it give
+    the factor between counter bytes and real bytes (it reads and writes COPY_BYTES)."""
+    import torch
+    src = torch.randint(0, 255, (COPY_BYTES,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "repeats": 5}))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel_call):
+    """HBM bytes per launch of a call's kernels from the committed counter summary, or None
+    when there is none or a kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("calls", {}).get(kernel_call)
+    if not entry:
+        return None
+    for src, digest in entry.get("sources", {}).items():
+        p = os.path.join(ROOT, src)
+        if not os.path.exists(p) or source_digest(p) != digest:
+            return None
+    return entry.get("bytes_per_launch")
 
 
 def stage_bytes(c, buf, d):
@@ -125,6 +170,9 @@ def cpu_baseline(w, p, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the hot path "
               "is a single-GPU kernel library and this build has no multi-GPU mode.",
@@ -212,7 +260,7 @@ def main():
     dom = max(per_stage_bytes, key=lambda k: per_stage_bytes[k])
     achieved = per_stage_bytes[dom] / (stage_ms[dom] * 1e-3)
     roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK, "traffic": None, "kernel": dom,
+                "frac": achieved / HBM_PEAK, "traffic": measured_traffic(dom), "kernel": dom,
                 "bytes_per_launch": per_stage_bytes[dom], "avg_launch_us": stage_ms[dom] * 1e3}
     step_s = graph_ms * 1e-3
     res = {

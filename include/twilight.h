@@ -36,7 +36,9 @@
  *
  * Paged cache layout (one contiguous block per (physical page, KV head)):
  *   k_cache, v_cache : fp16  [num_phys_pages, Hkv, 16, d]
- *   page_minmax      : fp16  [num_phys_pages, Hkv, 2, d]   row 0 = min, row 1 = max
+ *   page_minmax      : fp16  [B, Hkv, max_pages_per_seq, 2, d] in LOGICAL page order of
+ *                      each sequence, row 0 = min, row 1 = max (so one KV head's bounds are
+ *                      one contiguous stretch that the page scorer streams)
  *   k_codes          : uint8 [num_phys_pages, Hkv, 16, d/2] byte i = channel 2i in the
  *                      low nibble, channel 2i+1 in the high nibble
  *   k_meta           : fp16  [num_phys_pages, Hkv, 16, d/32, 2] {scale, zero} per group
@@ -90,7 +92,8 @@ int twilight_quantize_keys(const twl_layout_t* L, const void* k_cache,
 /* Quest per-page channelwise key bounds (atlas.scime.ai "Surprising findings": Quest
  * keeps per-page max-pooled key information). For every page holding a token at or after
  * token_begin[b] (NULL means 0), min and max of each channel over the page's valid tokens
- * (a partial last page uses only its seq_len-bounded tokens). */
+ * (a partial last page uses only its seq_len-bounded tokens), written at the page's
+ * logical position. Pages whose physical id is invalid are left untouched. */
 int quest_page_bounds(const twl_layout_t* L, const void* k_cache,
                       const int32_t* token_begin, void* page_minmax, hipStream_t stream);
 

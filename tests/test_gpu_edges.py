@@ -184,7 +184,7 @@ def test_append_one_token_updates_codes_and_bounds():
         assert np.array_equal(meta[..., 0].astype(np.float64), scale.astype(np.float64))
         lo, hi = oracle.page_bounds(k_all)
         P = lo.shape[0]
-        mm = mm_h[w.page_table[0, :P], g]
+        mm = mm_h[0, g, :P]
         assert np.array_equal(mm[:, 0].astype(np.float64), lo.astype(np.float64))
         assert np.array_equal(mm[:, 1].astype(np.float64), hi.astype(np.float64))
 

@@ -53,7 +53,7 @@ def test_full_size_step(name):
         cache_rows[(b, g)] = (
             c.k_codes[pages, g].cpu().numpy().reshape(-1, s.d // 2)[:n],
             c.k_meta[pages, g].cpu().numpy().reshape(-1, s.d // 32, 2)[:n],
-            None if c.page_minmax is None else c.page_minmax[pages, g].cpu().numpy())
+            None if c.page_minmax is None else c.page_minmax[b, g, :pages.numel()].cpu().numpy())
     del c, buf
     torch.cuda.empty_cache()
 

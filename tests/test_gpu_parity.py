@@ -75,7 +75,7 @@ def test_page_bounds_bit_exact(case):
     for (b, g), res in orc.items():
         n = int(w.seq_lens[b])
         P = -(-n // 16)
-        mm = host["page_minmax"][w.page_table[b, :P], g]          # [P, 2, d]
+        mm = host["page_minmax"][b, g, :P]                         # [P, 2, d]
         assert np.array_equal(mm[:, 0].astype(np.float64), res["lo"].astype(np.float64)), (b, g)
         assert np.array_equal(mm[:, 1].astype(np.float64), res["hi"].astype(np.float64)), (b, g)
 
