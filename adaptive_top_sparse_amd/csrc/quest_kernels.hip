@@ -113,8 +113,10 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
 // One 1024-thread block per (sequence, KV head); thread t owns pages [t*KPT, t*KPT+KPT).
 // Radix select over order-preserving 64-bit keys of the exact scores: the bits the keys
 // all share are skipped (block min/max), then 11-bit digits are examined from the top,
-// stopping as soon as the boundary bucket is taken whole; remaining exact ties go to the
-// lower page index. A block scan then compacts the chosen pages in page order.
+// stopping as soon as the boundary bucket is taken whole or holds at most 64 pages (one
+// wave then ranks those by score, then page index, and the last one taken becomes a
+// (score, page) threshold); more than 64 exact ties go to the lower page indices by a
+// block scan. A block scan then compacts the chosen pages in page order.
 template <int KPT>
 __global__ __launch_bounds__(1024) void quest_select_kernel(
     const double* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv,
@@ -125,6 +127,9 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   __shared__ uint32_t scan_lds[NT / kWave + 1];
   __shared__ uint64_t red64[NT / kWave], red64b[NT / kWave];
   __shared__ uint32_t pick[3];
+  __shared__ uint32_t n_short;
+  __shared__ uint64_t short_key[kWave + 1];
+  __shared__ int short_page[kWave + 1];
   TWL_PHASE(4);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
@@ -156,16 +161,24 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   TWL_PHASE(6);
 
   // bits above `top` are common to every key
-  uint64_t prefix, mask;
+  uint64_t prefix = 0, mask = 0;
   uint32_t rem = static_cast<uint32_t>(m);
-  bool all_eq_in = false;  // every key equal to the final prefix is selected
+  // how the boundary is decided: kTies = the first `rem` keys equal to the final prefix in
+  // page order; kAllIn = every key equal to the prefix; kPair = (key, page) >= (t_key, t_page)
+  // in the selection order (key descending, then page ascending)
+  enum { kTies, kAllIn, kPair } mode = kTies;
+  uint64_t t_key = 0;
+  int t_page = 0;
   if (kmin == kmax) {
-    prefix = kmax;
-    mask = ~0ull;
+    // every score ties: the first m pages
+    mode = kPair;
+    t_key = kmax;
+    t_page = m - 1;
   } else {
     int top = 63 - __clzll(kmin ^ kmax);
     mask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
     prefix = kmax & mask;
+    if (threadIdx.x == 0) n_short = 0u;
     int npass = 0;
     for (;;) {
       const int lo_bit = top >= 10 ? top - 10 : 0;
@@ -188,8 +201,53 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
       mask |= dmask << lo_bit;
       TWL_PHASE(7 + (npass < 4 ? npass : 4));
       ++npass;
-      if (cnt == rem) all_eq_in = true;
-      if (cnt == rem || lo_bit == 0) break;
+      if (cnt == rem) {
+        mode = kAllIn;
+        break;
+      }
+      if (cnt <= static_cast<uint32_t>(kWave)) {
+        // short boundary bucket: one wave ranks its pages in the selection order and the
+        // rem-th becomes the threshold pair
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          if (first + i < P && (key[i] & mask) == prefix) {
+            const uint32_t idx = atomicAdd(&n_short, 1u);
+            if (idx < static_cast<uint32_t>(kWave)) {  // always: idx < cnt <= 64
+              short_key[idx] = key[i];
+              short_page[idx] = first + i;
+            }
+          }
+        }
+        TWL_PHASE(14);
+        __syncthreads();
+        TWL_PHASE(15);
+        if (threadIdx.x < kWave) {
+          // lane l holds page l of the bucket; the loop broadcasts each with readlane
+          const int l = threadIdx.x;
+          const int n_in = __builtin_amdgcn_readfirstlane(static_cast<int>(cnt));
+          const bool live = l < n_in;
+          const uint64_t mk = live ? short_key[l] : 0ull;
+          const int mp = live ? short_page[l] : 0;
+          uint32_t rank = 0;
+          for (int j = 0; j < n_in; ++j) {
+            const uint64_t kj = readlane(mk, j);
+            const int pj = readlane(mp, j);
+            rank += (kj > mk || (kj == mk && pj < mp)) ? 1u : 0u;
+          }
+          if (live && rank == rem - 1) {
+            short_key[kWave] = mk;
+            short_page[kWave] = mp;
+          }
+        }
+        TWL_PHASE(16);
+        __syncthreads();
+        TWL_PHASE(17);
+        mode = kPair;
+        t_key = short_key[kWave];
+        t_page = short_page[kWave];
+        break;
+      }
+      if (lo_bit == 0) break;
       top = lo_bit - 1;
     }
   }
@@ -198,7 +256,7 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   // `rem` in page order are in (all of them unless exact ties remain)
   uint32_t tot;
   uint32_t eq_before = 0;
-  if (!all_eq_in) {
+  if (mode == kTies) {
     uint32_t n_eq = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
@@ -211,12 +269,16 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   for (int i = 0; i < KPT; ++i) {
     bool c = false;
     if (first + i < P) {
-      const uint64_t km = key[i] & mask;
-      if (km > prefix) {
-        c = true;
-      } else if (km == prefix) {
-        c = all_eq_in || eq_before < rem;
-        ++eq_before;
+      if (mode == kPair) {
+        c = key[i] > t_key || (key[i] == t_key && first + i <= t_page);
+      } else {
+        const uint64_t km = key[i] & mask;
+        if (km > prefix) {
+          c = true;
+        } else if (km == prefix) {
+          c = mode == kAllIn || eq_before < rem;
+          ++eq_before;
+        }
       }
     }
     chosen[i] = c;

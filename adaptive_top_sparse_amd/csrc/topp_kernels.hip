@@ -10,9 +10,18 @@
 //  * tau is the largest fp32 value with sum_{W_j >= tau} M_j >= ceil(p * sum_j M_j). The
 //    search narrows the range of fp32 bit patterns (monotone for W >= 0) with 2048-bucket
 //    mass histograms, instead of halving it once per pass: a 31-bit range closes in at
-//    most three passes, each one read of the registers.
-//  * Kept = {W_j >= tau, W_j > 0}, compacted with a block scan in slot order, which is
-//    ascending token order because candidate pages are ascending.
+//    most three passes. As soon as the boundary bucket holds at most 64 weights, they are
+//    gathered and one wave finishes the search over them directly.
+//  * W is read from memory once and stays resident for every pass: up to 32 values per
+//    lane in VGPRs, the rest (units above 32768 slots) in LDS.
+//  * Kept = {W_j >= tau, W_j > 0}, compacted in slot order (per-wave scans, then one
+//    exchange of wave totals), which is ascending token order because candidate pages are
+//    ascending.
+// When the group is large relative to the unit (G * slots-per-thread above 32), a wide
+// pass first forms W over many work-groups into the workspace, so that the per-unit block
+// does not stream G rows of weights through one CU.
+#include <type_traits>
+
 #include "twl_device.h"
 #include "twl_launch.h"
 
@@ -21,8 +30,15 @@ TWL_PHASE_STORAGE(topp)
 namespace twl {
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kToppThreads = 1024;
+constexpr int kToppWaves = kToppThreads / kWave;
 constexpr int kBins = 2048;
+constexpr int kRegVecs = 8;       // W vectors per lane held in VGPRs; the rest live in LDS
+constexpr int kDirectLoads = 32;  // largest G * slots-per-thread read straight from weights
+constexpr int kMeanThreads = 256;
+constexpr int kMeanSlots = kMeanThreads * 16;  // slots per work-group of the group-mean pass
 
 // floor(W * 2^(40 - e)) for a non-negative fp32 W given by its bits, e the binary exponent
 // of the unit's largest W: integer shifts of the 24-bit significand (W < 2^(e+1), so the
@@ -36,130 +52,204 @@ __device__ __forceinline__ uint64_t fixed_mass(uint32_t key, int e) {
   return sh <= -24 ? 0 : (sig >> (-sh));
 }
 
-// Each thread owns SPT consecutive slots. Up to 16 stay in registers for the whole search;
-// larger rows are processed as 16-slot tiles, with W staged once in the workspace (each
-// thread re-reads only what it wrote). A slot is a candidate when its page rank is below the
-// unit's candidate count and its token is inside the sequence; slots of unmapped pages
-// carry weight 0 from the estimate and are never kept (W > 0 is required).
-template <int SPT>
-__global__ __launch_bounds__(kToppThreads) void topp_kernel(
+template <int VW>
+__device__ __forceinline__ void load_vec(const float* p, float (&x)[VW]) {
+  if constexpr (VW == 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+    x[0] = t[0];
+    x[1] = t[1];
+    x[2] = t[2];
+    x[3] = t[3];
+  } else if constexpr (VW == 2) {
+    const f32x2 t = *reinterpret_cast<const f32x2*>(p);
+    x[0] = t[0];
+    x[1] = t[1];
+  } else {
+    x[0] = *p;
+  }
+}
+
+// Page id behind slot s0, loaded unconditionally (entry 0 stands in when the slot's page
+// rank is past the candidates) so that loads can be issued before any is used.
+__device__ __forceinline__ int page_id_of(const int32_t* cand_row, int cnt, int s0) {
+  if (cand_row == nullptr) return 0;
+  const int r = s0 / kPage;
+  return cand_row[r < cnt ? r : 0];
+}
+
+// Logical token of slot s0 (s0 a multiple of 4 or less, so its vector stays in one page)
+// given its page id from page_id_of, or -1 when the slot's page is not a candidate. Tokens
+// past seq_len are filtered by the caller.
+__device__ __forceinline__ int page_token(const int32_t* cand_row, int cnt, int max_pages,
+                                          int s0, int pid) {
+  if (cand_row == nullptr) return s0;
+  if (s0 / kPage >= cnt || pid < 0 || pid >= max_pages) return -1;
+  return pid * kPage + s0 % kPage;
+}
+
+// Candidate pages in the row of unit `unit` (0 without a page list).
+__device__ __forceinline__ int candidate_pages(const int32_t* cand_pages,
+                                               const int32_t* cand_count, long unit,
+                                               int cand_stride_pages, int n) {
+  if (cand_pages == nullptr) return 0;
+  int cnt = cand_count ? cand_count[unit] : (n + kPage - 1) / kPage;
+  return cnt < cand_stride_pages ? cnt : cand_stride_pages;
+}
+
+// Group mean of the weights on candidate slots (0 elsewhere), for units whose block would
+// otherwise read G rows alone. Work-group (chunk, g, b) covers kMeanSlots slots; each
+// thread four vectors of four, contiguous across the work-group.
+template <int G>
+__global__ __launch_bounds__(kMeanThreads) void topp_mean_kernel(
     const float* __restrict__ weights, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages,
-    const int32_t* __restrict__ seq_lens, int Hkv, int G, int max_pages, float p,
-    int32_t* __restrict__ kept, int32_t* __restrict__ kept_count, float* __restrict__ tau_out,
-    float* __restrict__ stage) {
-  constexpr int TILE = SPT < 16 ? SPT : 16;
-  constexpr int NT = SPT / TILE;
-  constexpr int PG = (TILE + kPage - 1) / kPage;  // candidate pages a tile touches
+    const int32_t* __restrict__ seq_lens, int Hkv, int max_pages, float* __restrict__ stage) {
+  const int b = blockIdx.z;
+  const int g = blockIdx.y;
+  const long unit = static_cast<long>(b) * Hkv + g;
+  const int n = seq_len_clamped(seq_lens, b, max_pages);
+  const int n_slots = cand_stride_pages * kPage;
+  const int32_t* cand_row = cand_pages ? cand_pages + unit * cand_stride_pages : nullptr;
+  const int cnt = candidate_pages(cand_pages, cand_count, unit, cand_stride_pages, n);
+  const float* row0 = weights + unit * G * n_slots;
+  const float inv_g = 1.0f / static_cast<float>(G);  // exact: G is a power of two
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int s0 = blockIdx.x * kMeanSlots + v * (kMeanThreads * 4) + threadIdx.x * 4;
+    const bool in_row = s0 < n_slots;
+    const int sl = in_row ? s0 : 0;  // loads stay unconditional (and in bounds)
+    float x[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) load_vec<4>(row0 + static_cast<long>(h) * n_slots + sl, x[h]);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += x[h][j];
+    const int t0 = page_token(cand_row, cnt, max_pages, sl, page_id_of(cand_row, cnt, sl));
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (t0 >= 0 && t0 + j < n) ? fmaxf(acc[j] * inv_g, 0.f) : 0.f;
+    if (in_row) *reinterpret_cast<f32x4*>(stage + unit * n_slots + s0) = w;
+  }
+}
+
+// Slot layout of a unit inside its block: wave w owns SPT*64 consecutive slots from
+// w*SPT*64; its vector v covers 64*VW consecutive slots, lane l holding VW of them from
+// v*64*VW + l*VW. Loads are contiguous across the wave, and slot order is
+// (wave, vector, lane, element), which the compaction keeps.
+template <int SPT>
+struct SlotMap {
+  static constexpr int VW = SPT < 4 ? SPT : 4;
+  static constexpr int NV = SPT / VW;
+  static constexpr int NR = NV < kRegVecs ? NV : kRegVecs;  // vectors in VGPRs
+  static constexpr int NL = NV - NR;                        // vectors in LDS (VW == 4)
+};
+
+// `src` holds G rows of n_slots values per unit: the estimate's weights, or (G == 1) the
+// group means formed by topp_mean_kernel, which are already 0 off the candidates.
+template <int G, int SPT>
+__global__ __launch_bounds__(kToppThreads) void topp_kernel(
+    const float* __restrict__ src, const int32_t* __restrict__ cand_pages,
+    const int32_t* __restrict__ cand_count, int cand_stride_pages,
+    const int32_t* __restrict__ seq_lens, int Hkv, int max_pages, float p,
+    int32_t* __restrict__ kept, int32_t* __restrict__ kept_count,
+    float* __restrict__ tau_out) {
+  using M = SlotMap<SPT>;
+  constexpr int VW = M::VW, NV = M::NV, NR = M::NR, NL = M::NL;
+  static_assert(NL == 0 || VW == 4, "LDS-resident vectors are four wide");
   __shared__ unsigned long long mass[kBins];
-  __shared__ uint32_t scan_u32[kToppThreads / kWave + 1], scan_u32b[kToppThreads / kWave];
-  __shared__ uint64_t red64[kToppThreads / kWave];
+  __shared__ f32x4 w_lds[NL > 0 ? NL * kToppThreads : 1];
+  __shared__ uint32_t red_a[kToppWaves], red_b[kToppWaves], wave_tot[kToppWaves];
+  __shared__ uint64_t red64[kToppWaves];
   __shared__ uint64_t pick[3];
+  __shared__ uint32_t n_short[2], short_keys[kWave + 1];
   TWL_PHASE(0);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
   const long unit = static_cast<long>(b) * Hkv + g;
-  const int Hq = Hkv * G;
   const int n = seq_len_clamped(seq_lens, b, max_pages);
   const int n_slots = cand_stride_pages * kPage;
   const int32_t* cand_row = cand_pages ? cand_pages + unit * cand_stride_pages : nullptr;
-  int cnt = 0;
-  if (cand_pages != nullptr) {
-    cnt = cand_count ? cand_count[unit] : (n + kPage - 1) / kPage;
-    cnt = cnt < cand_stride_pages ? cnt : cand_stride_pages;
-  }
-  const int first = threadIdx.x * SPT;
-  float* my_stage = NT > 1 ? stage + unit * n_slots + first : nullptr;
+  const int cnt = candidate_pages(cand_pages, cand_count, unit, cand_stride_pages, n);
+  const int lane = lane_id();
+  const int wv = threadIdx.x / kWave;
+  const int wbase = wv * SPT * kWave;
+  const float* row0 = src + unit * G * n_slots;
   const float inv_g = 1.0f / static_cast<float>(G);  // exact: G is a power of two
 
-  // logical token of the tile's slot i, or -1 (tile-local page ids preloaded in pg[])
-  auto token_of = [&](int f0, const int (&pg)[PG], int i) -> int {
-    const int slot = f0 + i;
-    if (slot >= n_slots) return -1;
-    int t;
-    if (cand_row == nullptr) {
-      t = slot;
-    } else {
-      const int pid = pg[(i + (f0 % kPage)) / kPage];
-      if (slot / kPage >= cnt || pid < 0) return -1;
-      t = pid * kPage + slot % kPage;
-    }
-    return t < n ? t : -1;
-  };
-  auto load_pages = [&](int f0, int (&pg)[PG]) {
-#pragma unroll
-    for (int j = 0; j < PG; ++j) {
-      const int r = f0 / kPage + j;
-      pg[j] = (cand_row != nullptr && r < cnt) ? cand_row[r] : -1;
-    }
-  };
-
-  // pass 0: W_j = mean of the group's weights on candidate slots (0 elsewhere)
-  float W[TILE];
+  // pass 0: W = mean of the group's weights on candidate slots (0 elsewhere). A batch of
+  // vectors first issues all its loads (weights and page ids), then forms W; n_slots is a
+  // multiple of 16, so a vector that starts inside the row ends inside it, and vectors past
+  // the row load slot 0 instead, so that no load sits behind a branch.
+  float W[NR][VW];
   uint32_t kmax = 0, kmin = 0xffffffffu;
-#pragma unroll 1
-  for (int t = 0; t < NT; ++t) {
-    const int f0 = first + t * TILE;
-    int pg[PG];
-    load_pages(f0, pg);
+  auto form_batch = [&](auto nb_tag, int v0, float (*dst)[VW]) {
+    constexpr int NB = decltype(nb_tag)::value;
+    float x[NB][G][VW];
+    int pid[NB];
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) W[i] = 0.f;
-    if (f0 < n_slots) {
-      for (int h = 0; h < G; ++h) {
-        const float* row = weights + (static_cast<long>(b) * Hq + g * G + h) * n_slots + f0;
-        if constexpr (TILE % 4 == 0) {
-          // n_slots % 16 == 0, so a tile that starts inside the row ends inside it
+    for (int i = 0; i < NB; ++i) {
+      const int s0 = wbase + (v0 + i) * kWave * VW + lane * VW;
+      const int sl = s0 < n_slots ? s0 : 0;
 #pragma unroll
-          for (int i = 0; i < TILE; i += 4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
-            W[i] += v[0];
-            W[i + 1] += v[1];
-            W[i + 2] += v[2];
-            W[i + 3] += v[3];
-          }
-        } else {
+      for (int h = 0; h < G; ++h)
+        load_vec<VW>(row0 + static_cast<long>(h) * n_slots + sl, x[i][h]);
+      pid[i] = page_id_of(cand_row, cnt, sl);
+    }
 #pragma unroll
-          for (int i = 0; i < TILE; ++i)
-            if (f0 + i < n_slots) W[i] += row[i];
+    for (int i = 0; i < NB; ++i) {
+      const int s0 = wbase + (v0 + i) * kWave * VW + lane * VW;
+      const int t0 = s0 < n_slots ? page_token(cand_row, cnt, max_pages, s0, pid[i]) : -1;
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc += x[i][h][j];
+        const float w = (t0 >= 0 && t0 + j < n) ? fmaxf(acc * inv_g, 0.f) : 0.f;
+        dst[i][j] = w;
+        const uint32_t k = __float_as_uint(w);
+        if (k > 0) {
+          kmax = k > kmax ? k : kmax;
+          kmin = k < kmin ? k : kmin;
         }
       }
     }
+  };
+  if constexpr (NL > 0) {
+    constexpr int kBatch = 4;
+    static_assert(NL % kBatch == 0, "LDS vectors come in batches of four");
+#pragma unroll 1
+    for (int v = 0; v < NL; v += kBatch) {
+      float w[kBatch][VW];
+      form_batch(std::integral_constant<int, kBatch>(), NR + v, w);
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) {
-      W[i] = token_of(f0, pg, i) >= 0 ? fmaxf(W[i] * inv_g, 0.f) : 0.f;
-      const uint32_t k = __float_as_uint(W[i]);
-      if (k > 0) {
-        kmax = k > kmax ? k : kmax;
-        kmin = k < kmin ? k : kmin;
-      }
-    }
-    if (NT > 1 && f0 < n_slots) {
-#pragma unroll
-      for (int i = 0; i < TILE; i += 4)
-        *reinterpret_cast<f32x4*>(my_stage + t * TILE + i) =
-            f32x4{W[i], W[i + 1], W[i + 2], W[i + 3]};
+      for (int i = 0; i < kBatch; ++i)
+        w_lds[(v + i) * kToppThreads + threadIdx.x] =
+            f32x4{w[i][0], w[i][1 % VW], w[i][2 % VW], w[i][3 % VW]};
     }
   }
+  // register vectors in batches of at most four, which bounds the loads held in flight
+  constexpr int kRegBatch = NR < 4 ? NR : 4;
+#pragma unroll
+  for (int v = 0; v < NR; v += kRegBatch) form_batch(std::integral_constant<int, kRegBatch>(), v, W + v);
   TWL_PHASE(1);
-  block_minmax<kToppThreads, uint32_t>(kmin, kmax, scan_u32, scan_u32b, 0xffffffffu, 0u, &kmin,
-                                       &kmax);
+  block_minmax<kToppThreads, uint32_t>(kmin, kmax, red_a, red_b, 0xffffffffu, 0u, &kmin, &kmax);
   TWL_PHASE(2);
 
-  // reload tile t of this thread's W (no-op when everything fits one tile)
-  auto load_tile = [&](int t) {
-    if constexpr (NT > 1) {
-      if (first + t * TILE < n_slots) {
+  // f(v, w) for every vector v of this lane's resident W, in vector order
+  auto for_each_w = [&](auto&& f) {
 #pragma unroll
-        for (int i = 0; i < TILE; i += 4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(my_stage + t * TILE + i);
-          W[i] = v[0];
-          W[i + 1] = v[1];
-          W[i + 2] = v[2];
-          W[i + 3] = v[3];
-        }
-      } else {
+    for (int v = 0; v < NR; ++v) f(v, W[v]);
+    if constexpr (NL > 0) {
+#pragma unroll 2
+      for (int v = 0; v < NL; ++v) {
+        const f32x4 t = w_lds[v * kToppThreads + threadIdx.x];
+        float w[VW];
 #pragma unroll
-        for (int i = 0; i < TILE; ++i) W[i] = 0.f;
+        for (int j = 0; j < VW; ++j) w[j] = t[j];
+        f(NR + v, w);
       }
     }
   };
@@ -182,20 +272,25 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
       const int shift = bits > 11 ? bits - 11 : 0;
       mass[threadIdx.x] = 0ull;
       mass[threadIdx.x + kToppThreads] = 0ull;
+      if (threadIdx.x == 0) n_short[pass_no & 1] = 0u;
       __syncthreads();
-#pragma unroll 1
-      for (int t = 0; t < NT; ++t) {
-        load_tile(t);
+      if (pass_no == 0) TWL_PHASE(12);
+      for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll
-        for (int i = 0; i < TILE; ++i) {
-          const uint32_t k = __float_as_uint(W[i]);
+        for (int j = 0; j < VW; ++j) {
+          const uint32_t k = __float_as_uint(w[j]);
           if (k >= lo && k <= hi) {
             const uint64_t m = fixed_mass(k, e);
             if (m != 0) atomicAdd(&mass[(k - lo) >> shift], m);
           }
         }
-      }
+        // keep the scheduler from forming every vector's 64-bit masses ahead of the
+        // atomics (which would need two VGPRs per slot)
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (pass_no == 0) TWL_PHASE(13);
       __syncthreads();
+      if (pass_no == 0) TWL_PHASE(14);
       uint64_t above, inb;
       const uint32_t bucket = block_pick_bucket<kToppThreads, uint64_t>(
           mass[2 * threadIdx.x], mass[2 * threadIdx.x + 1], rem, red64, pick, &above, &inb,
@@ -207,36 +302,85 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
       lo = nlo;
       hi = nhi;
       TWL_PHASE(4 + (pass_no < 4 ? pass_no : 4));
-      ++pass_no;
       if (shift == 0) break;
+      // Short boundary bucket: collect its keys and let one wave finish the search.
+      // tau is then the largest key whose mass together with every larger key of the
+      // bucket reaches rem (0 < rem <= the bucket's mass, so one exists).
+      const int par = pass_no & 1;
+      for_each_w([&](int, const float(&w)[VW]) {
+#pragma unroll
+        for (int j = 0; j < VW; ++j) {
+          const uint32_t k = __float_as_uint(w[j]);
+          if (k >= lo && k <= hi) {
+            const uint32_t idx = atomicAdd(&n_short[par], 1u);
+            if (idx < kWave) short_keys[idx] = k;
+          }
+        }
+      });
+      if (pass_no == 0) TWL_PHASE(15);
+      __syncthreads();
+      if (pass_no == 0) TWL_PHASE(16);
+      const uint32_t n_in = __builtin_amdgcn_readfirstlane(n_short[par]);
+      ++pass_no;
+      if (n_in > kWave) continue;
+      if (wv == 0) {
+        // lane i holds key i; the loop broadcasts each key and its mass with readlane
+        const bool live = lane < static_cast<int>(n_in);
+        const uint32_t my_key = live ? short_keys[lane] : 0u;
+        const uint64_t my_mass = live ? fixed_mass(my_key, e) : 0ull;
+        uint64_t s_ge = 0;  // mass of the bucket's keys >= my_key
+        for (uint32_t i = 0; i < n_in; ++i) {
+          const uint32_t ki = readlane(my_key, static_cast<int>(i));
+          const uint64_t mi = readlane(my_mass, static_cast<int>(i));
+          s_ge += ki >= my_key ? mi : 0ull;
+        }
+        const uint32_t cand = (live && s_ge >= rem) ? my_key : 0u;
+        const uint32_t best = wave_reduce(cand, OpMax());
+        if (lane == 0) short_keys[kWave] = best;
+      }
+      TWL_PHASE(17);
+      __syncthreads();
+      TWL_PHASE(18);
+      lo = short_keys[kWave];
+      break;
     }
     tau = __uint_as_float(lo);
   }
 
   TWL_PHASE(9);
-  // compaction in slot order
+  // compaction in slot order: wave totals first, then per-vector wave scans
   uint32_t nk = 0;
-#pragma unroll 1
-  for (int t = 0; t < NT; ++t) {
-    load_tile(t);
+  for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) nk += (W[i] > 0.f && W[i] >= tau) ? 1u : 0u;
+    for (int j = 0; j < VW; ++j) nk += (w[j] > 0.f && w[j] >= tau) ? 1u : 0u;
+  });
+  nk = wave_reduce(nk, OpSum());
+  if (lane == 0) wave_tot[wv] = nk;
+  __syncthreads();
+  uint32_t run = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kToppWaves; ++i) {
+    const uint32_t c = wave_tot[i];
+    run += i < wv ? c : 0u;
+    total += c;
   }
-  uint32_t total;
-  uint32_t pos = block_excl_scan_u32<kToppThreads>(nk, scan_u32, &total);
   TWL_PHASE(10);
   int32_t* out = kept + unit * n_slots;
-#pragma unroll 1
-  for (int t = 0; t < NT; ++t) {
-    const int f0 = first + t * TILE;
-    int pg[PG];
-    load_pages(f0, pg);
-    load_tile(t);
+  for_each_w([&](int v, const float(&w)[VW]) {
+    uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) {
-      if (W[i] > 0.f && W[i] >= tau) out[pos++] = token_of(f0, pg, i);
+    for (int j = 0; j < VW; ++j) c += (w[j] > 0.f && w[j] >= tau) ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (c != 0) {
+      const int s0 = wbase + v * kWave * VW + lane * VW;
+      const int t0 = page_token(cand_row, cnt, max_pages, s0, page_id_of(cand_row, cnt, s0));
+      uint32_t pos = run + incl - c;
+#pragma unroll
+      for (int j = 0; j < VW; ++j)
+        if (w[j] > 0.f && w[j] >= tau) out[pos++] = t0 + j;
     }
-  }
+    run += readlane(incl, kWave - 1);
+  });
   if (threadIdx.x == 0) {
     kept_count[unit] = static_cast<int32_t>(total);
     if (tau_out) tau_out[unit] = tau;
@@ -244,20 +388,72 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
   TWL_PHASE(11);
 }
 
+// Everything a launch needs besides the kernel's template arguments.
+struct ToppArgs {
+  const Layout* L;
+  const float* weights;
+  const int32_t* cand_pages;
+  const int32_t* cand_count;
+  int stride;
+  float p;
+  int32_t* kept;
+  int32_t* kept_count;
+  float* tau;
+  float* stage;
+  hipStream_t s;
+};
+
+template <int G, int SPT>
+void launch_main(const ToppArgs& a, const float* src) {
+  topp_kernel<G, SPT><<<dim3(a.L->Hkv, a.L->B), kToppThreads, 0, a.s>>>(
+      src, a.cand_pages, a.cand_count, a.stride, a.L->seq_lens, a.L->Hkv, a.L->max_pages, a.p,
+      a.kept, a.kept_count, a.tau);
+}
+
+template <int G>
+void launch_mean(const ToppArgs& a) {
+  const int n_slots = a.stride * kPage;
+  const dim3 grid((n_slots + kMeanSlots - 1) / kMeanSlots, a.L->Hkv, a.L->B);
+  topp_mean_kernel<G><<<grid, kMeanThreads, 0, a.s>>>(a.weights, a.cand_pages, a.cand_count,
+                                                      a.stride, a.L->seq_lens, a.L->Hkv,
+                                                      a.L->max_pages, a.stage);
+}
+
+bool uses_mean_pass(int G, int spt) { return G > 1 && G * spt > kDirectLoads; }
+
 template <int SPT>
-void topp_launch(const Layout& L, const float* weights, const int32_t* cand_pages,
-                 const int32_t* cand_count, int stride, float p, int32_t* kept,
-                 int32_t* kept_count, float* tau, float* stage, hipStream_t s) {
-  topp_kernel<SPT><<<dim3(L.Hkv, L.B), kToppThreads, 0, s>>>(
-      weights, cand_pages, cand_count, stride, L.seq_lens, L.Hkv, L.G(), L.max_pages, p, kept,
-      kept_count, tau, stage);
+void launch_spt(const ToppArgs& a) {
+  const int G = a.L->G();
+  if (uses_mean_pass(G, SPT)) {
+    if (G == 2) launch_mean<2>(a);
+    else if (G == 4) launch_mean<4>(a);
+    else launch_mean<8>(a);
+    launch_main<1, SPT>(a, a.stage);
+    return;
+  }
+  if (G == 1) {
+    launch_main<1, SPT>(a, a.weights);
+  } else if (G == 2) {
+    if constexpr (2 * SPT <= kDirectLoads) launch_main<2, SPT>(a, a.weights);
+  } else if (G == 4) {
+    if constexpr (4 * SPT <= kDirectLoads) launch_main<4, SPT>(a, a.weights);
+  } else {
+    if constexpr (8 * SPT <= kDirectLoads) launch_main<8, SPT>(a, a.weights);
+  }
+}
+
+int slots_per_thread(int cand_stride_pages) {
+  const int n_slots = cand_stride_pages * kPage;
+  int spt = 1;
+  while (spt * kToppThreads < n_slots) spt *= 2;
+  return spt;
 }
 
 }  // namespace
 
 size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages) {
+  if (!uses_mean_pass(L.G(), slots_per_thread(cand_stride_pages))) return 0;
   const long n_slots = static_cast<long>(cand_stride_pages) * kPage;
-  if (n_slots <= 16L * kToppThreads) return 0;
   return align_up(static_cast<size_t>(L.B) * L.Hkv * n_slots * sizeof(float), 256);
 }
 
@@ -265,16 +461,17 @@ hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* can
                        const int32_t* cand_count, int cand_stride_pages, float p,
                        int32_t* kept, int32_t* kept_count, float* tau, void* ws,
                        hipStream_t s) {
-  const int n_slots = cand_stride_pages * kPage;
-  const int spt = (n_slots + kToppThreads - 1) / kToppThreads;
-  float* st = static_cast<float*>(stage_scratch(ws, L));
-  if (spt <= 1) topp_launch<1>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
-  else if (spt <= 2) topp_launch<2>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
-  else if (spt <= 4) topp_launch<4>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
-  else if (spt <= 8) topp_launch<8>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
-  else if (spt <= 16) topp_launch<16>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
-  else if (spt <= 32) topp_launch<32>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
-  else topp_launch<64>(L, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau, st, s);
+  const ToppArgs a{&L, weights, cand_pages, cand_count, cand_stride_pages, p, kept,
+                   kept_count, tau, static_cast<float*>(stage_scratch(ws, L)), s};
+  switch (slots_per_thread(cand_stride_pages)) {
+    case 1: launch_spt<1>(a); break;
+    case 2: launch_spt<2>(a); break;
+    case 4: launch_spt<4>(a); break;
+    case 8: launch_spt<8>(a); break;
+    case 16: launch_spt<16>(a); break;
+    case 32: launch_spt<32>(a); break;
+    default: launch_spt<64>(a); break;
+  }
   return hipGetLastError();
 }
 

@@ -7,18 +7,21 @@
 #include "twl_launch.h"
 
 // Opt-in phase timing for tuning builds (-DTWL_PHASE_TIMING): work-group 0 / thread 0 of a
-// kernel stores the 100 MHz real-time clock at marked phase boundaries in a per-file device array that
+// kernel stores the 100 MHz real-time clock at marked phase boundaries (and the shader clock
+// counter at entry 32 + i) in a per-file device array that
 // an exported twl_phase_<file>() copies out. Compiled out otherwise.
 #ifdef TWL_PHASE_TIMING
 #define TWL_PHASE_STORAGE(NAME)                                                       \
-  static __device__ unsigned long long twl_phase_ts[32];                              \
+  static __device__ unsigned long long twl_phase_ts[64];                              \
   extern "C" void twl_phase_##NAME(unsigned long long* host) {                        \
     (void)hipMemcpyFromSymbol(host, HIP_SYMBOL(twl_phase_ts), sizeof(twl_phase_ts));  \
   }
 #define TWL_PHASE(i)                                                                   \
   do {                                                                                 \
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)     \
-      twl_phase_ts[i] = __builtin_amdgcn_s_memrealtime();                                  \
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {   \
+      twl_phase_ts[i] = __builtin_amdgcn_s_memrealtime();                              \
+      twl_phase_ts[32 + (i)] = __builtin_amdgcn_s_memtime();                           \
+    }                                                                                  \
   } while (0)
 // start and end clock of every work-group (linear id < 32768) and the XCC it ran on
 #define TWL_SPAN_STORAGE(NAME)                                                         \

@@ -23,6 +23,11 @@ CASES = {
     "cfg5s-p0.8": (5, dict(B=2, n=4096), 0.8),
     "cfg5s-p0.9": (5, dict(B=2, n=4096), 0.9),
     "cfg5s-p0.95": (5, dict(B=2, n=4096), 0.95),
+    # group means formed by the wide pass, then 16 slots per thread in VGPRs
+    "cfg5-n16k": (5, dict(B=1, n=16384 + 9), 0.9),
+    # units above 32768 slots keep half of W in LDS: GQA (wide pass) and MHA (direct)
+    "cfg5-n40k": (5, dict(B=1, n=40000 + 3), 0.9),
+    "cfg5-n40k-mha": (5, dict(B=1, n=40000 + 3, Hq=4, Hkv=4), 0.9),
 }
 
 
