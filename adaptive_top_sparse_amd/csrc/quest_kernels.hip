@@ -10,6 +10,8 @@
 // 2^53 of their finest step (always true for finite fp16 data of ordinary range) each fp64
 // FMA and add is exact, whatever the order. Exact scores make ties real ties; they are
 // broken by the lower page index.
+#include <type_traits>
+
 #include "twl_device.h"
 #include "twl_launch.h"
 
@@ -22,6 +24,12 @@ namespace {
 #ifndef TWL_SCORE_THREADS
 #define TWL_SCORE_THREADS 256
 #endif
+#ifndef TWL_SCORE_XCD_REMAP
+#define TWL_SCORE_XCD_REMAP 0
+#endif
+#ifndef TWL_SELECT_SMALL
+#define TWL_SELECT_SMALL 0
+#endif
 #ifndef TWL_SCORE_ROUNDS
 #define TWL_SCORE_ROUNDS 4
 #endif
@@ -32,80 +40,145 @@ constexpr int kScoreRounds = TWL_SCORE_ROUNDS;
 // covers kScoreThreads/LPP consecutive logical pages per round, kScoreRounds rounds, read
 // as one contiguous stretch of the KV head's bounds; all rounds' loads are issued before
 // any arithmetic, so each lane has 2 * rounds loads in flight.
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// Row stride of the score workspace: max_pages rounded up to a multiple of 64.
+__host__ __device__ inline long score_row_stride(int max_pages) {
+  return (static_cast<long>(max_pages) + 63) / 64 * 64;
+}
+
 template <int D>
 constexpr int score_pages_per_block() {
   return kScoreThreads / (D / 8) * kScoreRounds;
 }
 
-template <int D>
+// Sum of one value per round over the LPP lanes of a page, for 4 rounds at once: two
+// exchanges halve the values per lane (each lane keeping the rounds its bits select), then
+// a butterfly finishes. The partners differ by lane-index masks (LPP-1, LPP/2-1, then 2, 1
+// for LPP = 16, or 7, 2, 1 for LPP = 8) that span the page's lanes, so every lane ends with
+// the total of round round_of_lane(); fp64 adds of exact partial sums are exact in any
+// order.
+template <int LPP>
+__device__ __forceinline__ double reduce_rounds4(const double (&v)[4]) {
+  constexpr int kA = LPP == 16 ? kRowMirror : kRowHalfMirror;   // flips bit log2(LPP) - 1
+  constexpr int kB = LPP == 16 ? kRowHalfMirror : kQuadXor2;    // flips bit log2(LPP) - 2
+  const int lane = lane_id();
+  const bool ba = (lane & (LPP / 2)) != 0;
+  const bool bb = (lane & (LPP / 4)) != 0;
+  double h[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const double keep = ba ? v[2 * i + 1] : v[2 * i];
+    const double send = ba ? v[2 * i] : v[2 * i + 1];
+    h[i] = keep + dpp_any<kA>(send);
+  }
+  const double keep = bb ? h[1] : h[0];
+  const double send = bb ? h[0] : h[1];
+  double x = keep + dpp_any<kB>(send);
+  if constexpr (LPP == 16) x += dpp_any<kQuadXor2>(x);
+  x += dpp_any<kQuadXor1>(x);
+  return x;
+}
+
+// Round whose total reduce_rounds4 leaves in this lane, and whether the lane writes it.
+template <int LPP>
+__device__ __forceinline__ int round_of_lane() {
+  const int lane = lane_id();
+  return ((lane & (LPP / 2)) != 0 ? 1 : 0) + ((lane & (LPP / 4)) != 0 ? 2 : 0);
+}
+template <int LPP>
+__device__ __forceinline__ bool writes_round() {
+  return (lane_id() & (LPP / 4 - 1)) == 0;
+}
+
+template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ minmax,
-    const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int max_pages,
+    const int32_t* __restrict__ seq_lens, int Hkv, int max_pages,
     double* __restrict__ scores) {
   constexpr int LPP = D / 8;
   constexpr int PPI = kScoreThreads / LPP;  // pages per round
   constexpr int ROUNDS = kScoreRounds;
   constexpr int PPB = PPI * ROUNDS;
+  static_assert(ROUNDS == 4, "the round reduction handles four rounds");
   TWL_PHASE(0);
   TWL_SPAN_BEGIN();
   const int b = blockIdx.z;
-  const int g = blockIdx.y;
-  const int G = Hq / Hkv;
+  int bx = blockIdx.x, by = blockIdx.y;
+#if TWL_SCORE_XCD_REMAP
+  {
+    // work-groups are handed to the XCDs in turn; renumber them so that each XCD gets a
+    // contiguous share of the bounds (a permutation, so any placement stays correct)
+    const int nb = gridDim.x * gridDim.y;
+    if (nb % 8 == 0) {
+      const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+      const int rl = (lin % 8) * (nb / 8) + lin / 8;
+      bx = rl % gridDim.x;
+      by = rl / gridDim.x;
+    }
+  }
+#endif
+  const int g = by;
+  const int Hq = Hkv * G;
   const int n = seq_len_clamped(seq_lens, b, max_pages);
   const int P = (n + kPage - 1) / kPage;
-  const int p0 = blockIdx.x * PPB;
+  const int p0 = bx * PPB;
   if (p0 >= P) return;
   const int sub = threadIdx.x % LPP;
   const int c0 = sub * 8;
-  // this KV head's bounds, in logical page order
+  // this KV head's bounds, in logical page order; pages past the sequence load page p0
+  // (so that no load sits behind a branch) and are not written
   const uint16_t* unit_mm = minmax + (static_cast<long>(b) * Hkv + g) * max_pages * 2 * D;
   u32x4 lo[ROUNDS], hi[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int p = p0 + r * PPI + threadIdx.x / LPP;
-    if (p < P) {
-      const uint16_t* blk = unit_mm + static_cast<long>(p) * 2 * D + c0;
-      lo[r] = *reinterpret_cast<const u32x4*>(blk);
-      hi[r] = *reinterpret_cast<const u32x4*>(blk + D);
-    } else {
-      lo[r] = u32x4{0u, 0u, 0u, 0u};
-      hi[r] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const uint16_t* blk = unit_mm + static_cast<long>(p < P ? p : p0) * 2 * D + c0;
+    lo[r] = *reinterpret_cast<const u32x4*>(blk);
+    hi[r] = *reinterpret_cast<const u32x4*>(blk + D);
   }
+  // A_c / B_c: sums of the group's negative / non-negative q_hc, formed once per block
+  // (while the bounds are in flight) and read back per lane. Sums of at most 8 fp16 values
+  // are exact in fp64.
+  __shared__ double sA[D], sB[D];
+  if (threadIdx.x < D) {
+    const uint16_t* qh = q + (static_cast<long>(b) * Hq + g * G) * D + threadIdx.x;
+    double a = 0.0, bsum = 0.0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const double x = static_cast<double>(h2f(qh[h * D]));
+      a += fmin(x, 0.0);
+      bsum += fmax(x, 0.0);
+    }
+    sA[threadIdx.x] = a;
+    sB[threadIdx.x] = bsum;
+  }
+  __syncthreads();
   double A[8], Bc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    A[c] = 0.0;
-    Bc[c] = 0.0;
-  }
-  for (int h = 0; h < G; ++h) {
-    const u32x4 qv =
-        *reinterpret_cast<const u32x4*>(q + (static_cast<long>(b) * Hq + g * G + h) * D + c0);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint16_t bits = static_cast<uint16_t>((qv[c / 2] >> (16 * (c % 2))) & 0xffffu);
-      const double x = static_cast<double>(h2f(bits));
-      if (x < 0.0) A[c] += x; else Bc[c] += x;
-    }
+    A[c] = sA[c0 + c];
+    Bc[c] = sB[c0 + c];
   }
   TWL_PHASE(1);
-  double* out = scores + (static_cast<long>(b) * Hkv + g) * max_pages;
+  double part[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    double acc = 0.0;
+    double acc_lo = 0.0, acc_hi = 0.0;  // two chains per round
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int sh = 16 * (c % 2);
       const double l = static_cast<double>(h2f(static_cast<uint16_t>((lo[r][c / 2] >> sh) & 0xffffu)));
       const double u = static_cast<double>(h2f(static_cast<uint16_t>((hi[r][c / 2] >> sh) & 0xffffu)));
-      acc = fma(l, A[c], acc);
-      acc = fma(u, Bc[c], acc);
+      acc_lo = fma(l, A[c], acc_lo);
+      acc_hi = fma(u, Bc[c], acc_hi);
     }
-#pragma unroll
-    for (int o = LPP / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    const int p = p0 + r * PPI + threadIdx.x / LPP;
-    if (sub == 0 && p < P) out[p] = acc;
+    part[r] = acc_lo + acc_hi;
   }
+  const double total = reduce_rounds4<LPP>(part);
+  const int p = p0 + round_of_lane<LPP>() * PPI + threadIdx.x / LPP;
+  if (writes_round<LPP>() && p < P)
+    scores[(static_cast<long>(b) * Hkv + g) * score_row_stride(max_pages) + p] = total;
   TWL_PHASE(2);
   TWL_SPAN_END();
 }
@@ -117,12 +190,15 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
 // wave then ranks those by score, then page index, and the last one taken becomes a
 // (score, page) threshold); more than 64 exact ties go to the lower page indices by a
 // block scan. A block scan then compacts the chosen pages in page order.
-template <int KPT>
-__global__ __launch_bounds__(1024) void quest_select_kernel(
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void quest_select_kernel(
     const double* __restrict__ scores, const int32_t* __restrict__ seq_lens, int Hkv,
     int max_pages, int budget, int32_t* __restrict__ sel_pages, int32_t* __restrict__ sel_count) {
-  constexpr int NT = 1024;
-  constexpr int kBins = 2 * NT;
+  constexpr int kBins = 2048;
+  constexpr int BPT = kBins / NT;
+  constexpr int NW = NT / kWave;
+  // digit histogram, digit d at bucket_slot<NT, BPT>(d); after a pass has picked its digit
+  // it doubles as scratch for the short-bucket finish
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t scan_lds[NT / kWave + 1];
   __shared__ uint64_t red64[NT / kWave], red64b[NT / kWave];
@@ -143,14 +219,29 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
     for (int i = threadIdx.x; i < P; i += NT) out[i] = i;
     return;
   }
-  const double* sc = scores + unit * max_pages;
+  const double* sc = scores + unit * score_row_stride(max_pages);
   const int first = threadIdx.x * KPT;
   uint64_t key[KPT];
   uint64_t kmin = ~0ull, kmax = 0ull;
+  // pairs of scores in 16-byte loads, all issued before any is used: rows are padded to an
+  // even stride, and pairs that start past the sequence load entry 0 instead
+  constexpr int VW = KPT < 2 ? 1 : 2;
+  double sv[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; i += VW) {
+    const int pl = first + i < P ? first + i : 0;
+    if constexpr (VW == 2) {
+      const f64x2 v = *reinterpret_cast<const f64x2*>(sc + pl);
+      sv[i] = v[0];
+      sv[i + 1] = v[1];
+    } else {
+      sv[i] = sc[pl];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int p = first + i;
-    key[i] = p < P ? f64_order_key(sc[p]) : 0ull;
+    key[i] = p < P ? f64_order_key(sv[i]) : 0ull;
     if (p < P) {
       kmin = key[i] < kmin ? key[i] : kmin;
       kmax = key[i] > kmax ? key[i] : kmax;
@@ -179,23 +270,24 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
     mask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
     prefix = kmax & mask;
     if (threadIdx.x == 0) n_short = 0u;
-    int npass = 0;
+    [[maybe_unused]] int npass = 0;
     for (;;) {
       const int lo_bit = top >= 10 ? top - 10 : 0;
       const int nbits = top - lo_bit + 1;
       const uint64_t dmask = (1ull << nbits) - 1ull;
-      hist[threadIdx.x] = 0;
-      hist[threadIdx.x + NT] = 0;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) hist[i * NT + threadIdx.x] = 0;
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         if (first + i < P && (key[i] & mask) == prefix)
-          atomicAdd(&hist[(key[i] >> lo_bit) & dmask], 1u);
+          atomicAdd(&hist[bucket_slot<NT, BPT>(static_cast<uint32_t>((key[i] >> lo_bit) & dmask))],
+                    1u);
       }
       __syncthreads();
       uint32_t above, cnt;
-      const uint32_t digit = block_pick_bucket<NT, uint32_t>(
-          hist[2 * threadIdx.x], hist[2 * threadIdx.x + 1], rem, scan_lds, pick, &above, &cnt);
+      const uint32_t digit = block_pick_bucket_lds<NT, BPT, uint32_t>(hist, rem, scan_lds, pick,
+                                                                      &above, &cnt);
       rem -= above;
       prefix |= static_cast<uint64_t>(digit) << lo_bit;
       mask |= dmask << lo_bit;
@@ -221,25 +313,39 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
         TWL_PHASE(14);
         __syncthreads();
         TWL_PHASE(15);
-        if (threadIdx.x < kWave) {
-          // lane l holds page l of the bucket; the loop broadcasts each with readlane
-          const int l = threadIdx.x;
-          const int n_in = __builtin_amdgcn_readfirstlane(static_cast<int>(cnt));
+        {
+          // page i = lane; wave w counts the bucket's pages in its share that come before
+          // page i in the selection order, then wave 0 totals the shares
+          constexpr int JPW = kWave / NW;
+          uint32_t* part = hist;  // free until the next pass clears it
+          const int l = lane_id();
+          const int wv = threadIdx.x / kWave;
+          const int n_in = static_cast<int>(cnt);
           const bool live = l < n_in;
           const uint64_t mk = live ? short_key[l] : 0ull;
           const int mp = live ? short_page[l] : 0;
-          uint32_t rank = 0;
-          for (int j = 0; j < n_in; ++j) {
-            const uint64_t kj = readlane(mk, j);
-            const int pj = readlane(mp, j);
-            rank += (kj > mk || (kj == mk && pj < mp)) ? 1u : 0u;
+          uint32_t r_part = 0;
+#pragma unroll
+          for (int q = 0; q < JPW; ++q) {
+            const int j = wv * JPW + q;
+            const int jj = j < kWave ? j : 0;
+            const uint64_t kj = short_key[jj];
+            const int pj = short_page[jj];
+            r_part += (j < n_in && (kj > mk || (kj == mk && pj < mp))) ? 1u : 0u;
           }
-          if (live && rank == rem - 1) {
-            short_key[kWave] = mk;
-            short_page[kWave] = mp;
+          part[wv * kWave + l] = r_part;
+          TWL_PHASE(16);
+          __syncthreads();
+          if (wv == 0) {
+            uint32_t rank = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) rank += part[w2 * kWave + l];
+            if (live && rank == rem - 1) {
+              short_key[kWave] = mk;
+              short_page[kWave] = mp;
+            }
           }
         }
-        TWL_PHASE(16);
         __syncthreads();
         TWL_PHASE(17);
         mode = kPair;
@@ -292,18 +398,19 @@ __global__ __launch_bounds__(1024) void quest_select_kernel(
   TWL_PHASE(13);
 }
 
-template <int KPT>
+template <int NT, int KPT>
 void select_launch(const Layout& L, int budget, int32_t* sel_pages, int32_t* sel_count,
                    const double* scores, hipStream_t s) {
-  quest_select_kernel<KPT><<<dim3(L.Hkv, L.B), 1024, 0, s>>>(scores, L.seq_lens, L.Hkv,
-                                                             L.max_pages, budget, sel_pages,
-                                                             sel_count);
+  quest_select_kernel<NT, KPT><<<dim3(L.Hkv, L.B), NT, 0, s>>>(scores, L.seq_lens, L.Hkv,
+                                                               L.max_pages, budget, sel_pages,
+                                                               sel_count);
 }
 
 }  // namespace
 
 size_t quest_workspace_bytes(const Layout& L) {
-  return align_up(static_cast<size_t>(L.B) * L.Hkv * L.max_pages * sizeof(double), 256);
+  return align_up(static_cast<size_t>(L.B) * L.Hkv * score_row_stride(L.max_pages) * sizeof(double),
+                  256);
 }
 
 hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
@@ -311,26 +418,46 @@ hipError_t launch_quest_select(const Layout& L, const void* q, const void* minma
   double* scores = static_cast<double*>(stage_scratch(ws, L));
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* mm = static_cast<const uint16_t*>(minmax);
-  if (L.d == 128) {
-    constexpr int ppb = score_pages_per_block<128>();
+  auto score = [&](auto d_tag, auto g_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    constexpr int G = decltype(g_tag)::value;
+    constexpr int ppb = score_pages_per_block<D>();
     const dim3 grid((L.max_pages + ppb - 1) / ppb, L.Hkv, L.B);
-    quest_score_kernel<128><<<grid, kScoreThreads, 0, s>>>(qq, mm, L.seq_lens, L.Hq, L.Hkv,
-                                                           L.max_pages, scores);
-  } else {
-    constexpr int ppb = score_pages_per_block<64>();
-    const dim3 grid((L.max_pages + ppb - 1) / ppb, L.Hkv, L.B);
-    quest_score_kernel<64><<<grid, kScoreThreads, 0, s>>>(qq, mm, L.seq_lens, L.Hq, L.Hkv,
-                                                          L.max_pages, scores);
-  }
+    quest_score_kernel<D, G><<<grid, kScoreThreads, 0, s>>>(qq, mm, L.seq_lens, L.Hkv,
+                                                            L.max_pages, scores);
+  };
+  auto score_d = [&](auto d_tag) {
+    switch (L.G()) {
+      case 1: score(d_tag, std::integral_constant<int, 1>()); break;
+      case 2: score(d_tag, std::integral_constant<int, 2>()); break;
+      case 4: score(d_tag, std::integral_constant<int, 4>()); break;
+      default: score(d_tag, std::integral_constant<int, 8>()); break;
+    }
+  };
+  if (L.d == 128) score_d(std::integral_constant<int, 128>());
+  else score_d(std::integral_constant<int, 64>());
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int kpt_needed = (L.max_pages + 1023) / 1024;
-  if (kpt_needed <= 1) select_launch<1>(L, budget, sel_pages, sel_count, scores, s);
-  else if (kpt_needed <= 2) select_launch<2>(L, budget, sel_pages, sel_count, scores, s);
-  else if (kpt_needed <= 4) select_launch<4>(L, budget, sel_pages, sel_count, scores, s);
-  else if (kpt_needed <= 8) select_launch<8>(L, budget, sel_pages, sel_count, scores, s);
-  else if (kpt_needed <= 16) select_launch<16>(L, budget, sel_pages, sel_count, scores, s);
-  else select_launch<32>(L, budget, sel_pages, sel_count, scores, s);
+#if TWL_SELECT_SMALL > 0
+  // a tuning option, off by default: 256 threads (one wave per SIMD) up to this many pages
+  if (L.max_pages <= TWL_SELECT_SMALL) {
+    const int kpt = (L.max_pages + 255) / 256;
+    if (kpt <= 1) select_launch<256, 1>(L, budget, sel_pages, sel_count, scores, s);
+    else if (kpt <= 2) select_launch<256, 2>(L, budget, sel_pages, sel_count, scores, s);
+    else if (kpt <= 4) select_launch<256, 4>(L, budget, sel_pages, sel_count, scores, s);
+    else if (kpt <= 8) select_launch<256, 8>(L, budget, sel_pages, sel_count, scores, s);
+    else if (kpt <= 16) select_launch<256, 16>(L, budget, sel_pages, sel_count, scores, s);
+    else select_launch<256, 32>(L, budget, sel_pages, sel_count, scores, s);
+    return hipGetLastError();
+  }
+#endif
+  const int kpt = (L.max_pages + 1023) / 1024;
+  if (kpt <= 1) select_launch<1024, 1>(L, budget, sel_pages, sel_count, scores, s);
+  else if (kpt <= 2) select_launch<1024, 2>(L, budget, sel_pages, sel_count, scores, s);
+  else if (kpt <= 4) select_launch<1024, 4>(L, budget, sel_pages, sel_count, scores, s);
+  else if (kpt <= 8) select_launch<1024, 8>(L, budget, sel_pages, sel_count, scores, s);
+  else if (kpt <= 16) select_launch<1024, 16>(L, budget, sel_pages, sel_count, scores, s);
+  else select_launch<1024, 32>(L, budget, sel_pages, sel_count, scores, s);
   return hipGetLastError();
 }
 

@@ -17,7 +17,8 @@
 //  * Kept = {W_j >= tau, W_j > 0}, compacted in slot order (per-wave scans, then one
 //    exchange of wave totals), which is ascending token order because candidate pages are
 //    ascending.
-// When the group is large relative to the unit (G * slots-per-thread above 32), a wide
+// When the group is large relative to the unit (G * slots-per-thread above what one
+// block's registers take, 128 or 32), a wide
 // pass first forms W over many work-groups into the workspace, so that the per-unit block
 // does not stream G rows of weights through one CU.
 #include <type_traits>
@@ -32,13 +33,28 @@ namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kToppThreads = 1024;
-constexpr int kToppWaves = kToppThreads / kWave;
 constexpr int kBins = 2048;
-constexpr int kRegVecs = 8;       // W vectors per lane held in VGPRs; the rest live in LDS
-constexpr int kDirectLoads = 32;  // largest G * slots-per-thread read straight from weights
+// Units up to this many slots use 256-thread blocks (a tuning option, off by default: with
+// one wave per SIMD the longer per-lane code is slower than four waves sharing a SIMD).
+#ifndef TWL_TOPP_SMALL_UNIT
+#define TWL_TOPP_SMALL_UNIT 0
+#endif
+constexpr int kSmallUnit = TWL_TOPP_SMALL_UNIT;
 constexpr int kMeanThreads = 256;
 constexpr int kMeanSlots = kMeanThreads * 16;  // slots per work-group of the group-mean pass
+
+// Per block size: W vectors per lane held in VGPRs (the rest live in LDS) and the largest
+// G * slots-per-thread read straight from the weights. A 256-thread block has one wave per
+// SIMD and up to 512 VGPRs per lane, so it keeps a whole 8192-slot unit in registers and
+// issues all of its loads at once; a 1024-thread block has 128.
+template <int NT>
+struct ToppShape {
+  static constexpr int kWaves = NT / kWave;
+  static constexpr int kRegVecs = 8;
+  static constexpr int kDirectLoads = NT == 256 ? 128 : 32;
+  static constexpr int kRegBatch = NT == 256 ? 8 : 4;  // vectors whose loads go out together
+  static constexpr int kBpt = kBins / NT;              // histogram buckets per thread
+};
 
 // floor(W * 2^(40 - e)) for a non-negative fp32 W given by its bits, e the binary exponent
 // of the unit's largest W: integer shifts of the 24-bit significand (W < 2^(e+1), so the
@@ -139,30 +155,34 @@ __global__ __launch_bounds__(kMeanThreads) void topp_mean_kernel(
 // w*SPT*64; its vector v covers 64*VW consecutive slots, lane l holding VW of them from
 // v*64*VW + l*VW. Loads are contiguous across the wave, and slot order is
 // (wave, vector, lane, element), which the compaction keeps.
-template <int SPT>
+template <int NT, int SPT>
 struct SlotMap {
   static constexpr int VW = SPT < 4 ? SPT : 4;
   static constexpr int NV = SPT / VW;
-  static constexpr int NR = NV < kRegVecs ? NV : kRegVecs;  // vectors in VGPRs
-  static constexpr int NL = NV - NR;                        // vectors in LDS (VW == 4)
+  static constexpr int NR = NV < ToppShape<NT>::kRegVecs ? NV : ToppShape<NT>::kRegVecs;
+  static constexpr int NL = NV - NR;  // vectors in LDS (VW == 4)
 };
 
 // `src` holds G rows of n_slots values per unit: the estimate's weights, or (G == 1) the
 // group means formed by topp_mean_kernel, which are already 0 off the candidates.
-template <int G, int SPT>
-__global__ __launch_bounds__(kToppThreads) void topp_kernel(
+template <int NT, int G, int SPT>
+__global__ __launch_bounds__(NT) void topp_kernel(
     const float* __restrict__ src, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages,
     const int32_t* __restrict__ seq_lens, int Hkv, int max_pages, float p,
     int32_t* __restrict__ kept, int32_t* __restrict__ kept_count,
     float* __restrict__ tau_out) {
-  using M = SlotMap<SPT>;
+  using M = SlotMap<NT, SPT>;
+  using S = ToppShape<NT>;
   constexpr int VW = M::VW, NV = M::NV, NR = M::NR, NL = M::NL;
+  constexpr int NW = S::kWaves, BPT = S::kBpt;
   static_assert(NL == 0 || VW == 4, "LDS-resident vectors are four wide");
-  __shared__ unsigned long long mass[kBins];
-  __shared__ f32x4 w_lds[NL > 0 ? NL * kToppThreads : 1];
-  __shared__ uint32_t red_a[kToppWaves], red_b[kToppWaves], wave_tot[kToppWaves];
-  __shared__ uint64_t red64[kToppWaves];
+  // the mass histogram, bucket b at bucket_slot<NT, BPT>(b); after a pass has picked its
+  // bucket it doubles as scratch for the short-bucket finish
+  __shared__ uint64_t mass[kBins];
+  __shared__ f32x4 w_lds[NL > 0 ? NL * NT : 1];
+  __shared__ uint32_t red_a[NW], red_b[NW], wave_tot[NW];
+  __shared__ uint64_t red64[NW];
   __shared__ uint64_t pick[3];
   __shared__ uint32_t n_short[2], short_keys[kWave + 1];
   TWL_PHASE(0);
@@ -226,16 +246,17 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
       form_batch(std::integral_constant<int, kBatch>(), NR + v, w);
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
-        w_lds[(v + i) * kToppThreads + threadIdx.x] =
+        w_lds[(v + i) * NT + threadIdx.x] =
             f32x4{w[i][0], w[i][1 % VW], w[i][2 % VW], w[i][3 % VW]};
     }
   }
-  // register vectors in batches of at most four, which bounds the loads held in flight
-  constexpr int kRegBatch = NR < 4 ? NR : 4;
+  // register vectors in batches, which bounds the loads held in flight
+  constexpr int kRegBatch = NR < S::kRegBatch ? NR : S::kRegBatch;
 #pragma unroll
-  for (int v = 0; v < NR; v += kRegBatch) form_batch(std::integral_constant<int, kRegBatch>(), v, W + v);
+  for (int v = 0; v < NR; v += kRegBatch)
+    form_batch(std::integral_constant<int, kRegBatch>(), v, W + v);
   TWL_PHASE(1);
-  block_minmax<kToppThreads, uint32_t>(kmin, kmax, red_a, red_b, 0xffffffffu, 0u, &kmin, &kmax);
+  block_minmax<NT, uint32_t>(kmin, kmax, red_a, red_b, 0xffffffffu, 0u, &kmin, &kmax);
   TWL_PHASE(2);
 
   // f(v, w) for every vector v of this lane's resident W, in vector order
@@ -245,7 +266,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
     if constexpr (NL > 0) {
 #pragma unroll 2
       for (int v = 0; v < NL; ++v) {
-        const f32x4 t = w_lds[v * kToppThreads + threadIdx.x];
+        const f32x4 t = w_lds[v * NT + threadIdx.x];
         float w[VW];
 #pragma unroll
         for (int j = 0; j < VW; ++j) w[j] = t[j];
@@ -270,8 +291,8 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
       const uint32_t range = hi - lo;
       const int bits = range == 0 ? 0 : 32 - __clz(range);
       const int shift = bits > 11 ? bits - 11 : 0;
-      mass[threadIdx.x] = 0ull;
-      mass[threadIdx.x + kToppThreads] = 0ull;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) mass[i * NT + threadIdx.x] = 0ull;
       if (threadIdx.x == 0) n_short[pass_no & 1] = 0u;
       __syncthreads();
       if (pass_no == 0) TWL_PHASE(12);
@@ -281,7 +302,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
           const uint32_t k = __float_as_uint(w[j]);
           if (k >= lo && k <= hi) {
             const uint64_t m = fixed_mass(k, e);
-            if (m != 0) atomicAdd(&mass[(k - lo) >> shift], m);
+            if (m != 0) atomicAdd(&mass[bucket_slot<NT, BPT>((k - lo) >> shift)], m);
           }
         }
         // keep the scheduler from forming every vector's 64-bit masses ahead of the
@@ -292,9 +313,8 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
       __syncthreads();
       if (pass_no == 0) TWL_PHASE(14);
       uint64_t above, inb;
-      const uint32_t bucket = block_pick_bucket<kToppThreads, uint64_t>(
-          mass[2 * threadIdx.x], mass[2 * threadIdx.x + 1], rem, red64, pick, &above, &inb,
-          pass_no == 0 ? p : 0.f, &rem);
+      const uint32_t bucket = block_pick_bucket_lds<NT, BPT, uint64_t>(
+          mass, rem, red64, pick, &above, &inb, pass_no == 0 ? p : 0.f, &rem);
       rem -= above;
       const uint32_t nlo = lo + (bucket << shift);
       const uint32_t span = (1u << shift) - 1u;
@@ -323,22 +343,32 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
       const uint32_t n_in = __builtin_amdgcn_readfirstlane(n_short[par]);
       ++pass_no;
       if (n_in > kWave) continue;
-      if (wv == 0) {
-        // lane i holds key i; the loop broadcasts each key and its mass with readlane
+      {
+        // element i = lane; wave w adds the masses of its share of the bucket's keys that
+        // are >= key i, then wave 0 totals the shares
+        constexpr int JPW = kWave / NW;
+        uint64_t* part = mass;  // free until the next pass clears it
         const bool live = lane < static_cast<int>(n_in);
         const uint32_t my_key = live ? short_keys[lane] : 0u;
-        const uint64_t my_mass = live ? fixed_mass(my_key, e) : 0ull;
-        uint64_t s_ge = 0;  // mass of the bucket's keys >= my_key
-        for (uint32_t i = 0; i < n_in; ++i) {
-          const uint32_t ki = readlane(my_key, static_cast<int>(i));
-          const uint64_t mi = readlane(my_mass, static_cast<int>(i));
-          s_ge += ki >= my_key ? mi : 0ull;
+        uint64_t s_part = 0;
+#pragma unroll
+        for (int q = 0; q < JPW; ++q) {
+          const int j = wv * JPW + q;
+          const uint32_t kj = short_keys[j < kWave ? j : 0];
+          s_part += (j < static_cast<int>(n_in) && kj >= my_key) ? fixed_mass(kj, e) : 0ull;
         }
-        const uint32_t cand = (live && s_ge >= rem) ? my_key : 0u;
-        const uint32_t best = wave_reduce(cand, OpMax());
-        if (lane == 0) short_keys[kWave] = best;
+        part[wv * kWave + lane] = s_part;
+        TWL_PHASE(17);
+        __syncthreads();
+        if (wv == 0) {
+          uint64_t s_ge = 0;  // mass of the bucket's keys >= my_key
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) s_ge += part[w2 * kWave + lane];
+          const uint32_t cand = (live && s_ge >= rem) ? my_key : 0u;
+          const uint32_t best = wave_reduce(cand, OpMax());
+          if (lane == 0) short_keys[kWave] = best;
+        }
       }
-      TWL_PHASE(17);
       __syncthreads();
       TWL_PHASE(18);
       lo = short_keys[kWave];
@@ -359,7 +389,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(
   __syncthreads();
   uint32_t run = 0, total = 0;
 #pragma unroll
-  for (int i = 0; i < kToppWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const uint32_t c = wave_tot[i];
     run += i < wv ? c : 0u;
     total += c;
@@ -403,9 +433,9 @@ struct ToppArgs {
   hipStream_t s;
 };
 
-template <int G, int SPT>
+template <int NT, int G, int SPT>
 void launch_main(const ToppArgs& a, const float* src) {
-  topp_kernel<G, SPT><<<dim3(a.L->Hkv, a.L->B), kToppThreads, 0, a.s>>>(
+  topp_kernel<NT, G, SPT><<<dim3(a.L->Hkv, a.L->B), NT, 0, a.s>>>(
       src, a.cand_pages, a.cand_count, a.stride, a.L->seq_lens, a.L->Hkv, a.L->max_pages, a.p,
       a.kept, a.kept_count, a.tau);
 }
@@ -419,41 +449,48 @@ void launch_mean(const ToppArgs& a) {
                                                       a.L->max_pages, a.stage);
 }
 
-bool uses_mean_pass(int G, int spt) { return G > 1 && G * spt > kDirectLoads; }
+int block_threads(int n_slots) { return n_slots <= kSmallUnit ? 256 : 1024; }
 
-template <int SPT>
+int slots_per_thread(int n_slots) {
+  const int nt = block_threads(n_slots);
+  int spt = 1;
+  while (spt * nt < n_slots) spt *= 2;
+  return spt;
+}
+
+bool uses_mean_pass(int G, int n_slots) {
+  const int direct = block_threads(n_slots) == 256 ? ToppShape<256>::kDirectLoads
+                                                   : ToppShape<1024>::kDirectLoads;
+  return G > 1 && G * slots_per_thread(n_slots) > direct;
+}
+
+template <int NT, int SPT>
 void launch_spt(const ToppArgs& a) {
   const int G = a.L->G();
-  if (uses_mean_pass(G, SPT)) {
+  if (uses_mean_pass(G, a.stride * kPage)) {
     if (G == 2) launch_mean<2>(a);
     else if (G == 4) launch_mean<4>(a);
     else launch_mean<8>(a);
-    launch_main<1, SPT>(a, a.stage);
+    launch_main<NT, 1, SPT>(a, a.stage);
     return;
   }
+  constexpr int kDirect = ToppShape<NT>::kDirectLoads;
   if (G == 1) {
-    launch_main<1, SPT>(a, a.weights);
+    launch_main<NT, 1, SPT>(a, a.weights);
   } else if (G == 2) {
-    if constexpr (2 * SPT <= kDirectLoads) launch_main<2, SPT>(a, a.weights);
+    if constexpr (2 * SPT <= kDirect) launch_main<NT, 2, SPT>(a, a.weights);
   } else if (G == 4) {
-    if constexpr (4 * SPT <= kDirectLoads) launch_main<4, SPT>(a, a.weights);
+    if constexpr (4 * SPT <= kDirect) launch_main<NT, 4, SPT>(a, a.weights);
   } else {
-    if constexpr (8 * SPT <= kDirectLoads) launch_main<8, SPT>(a, a.weights);
+    if constexpr (8 * SPT <= kDirect) launch_main<NT, 8, SPT>(a, a.weights);
   }
-}
-
-int slots_per_thread(int cand_stride_pages) {
-  const int n_slots = cand_stride_pages * kPage;
-  int spt = 1;
-  while (spt * kToppThreads < n_slots) spt *= 2;
-  return spt;
 }
 
 }  // namespace
 
 size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages) {
-  if (!uses_mean_pass(L.G(), slots_per_thread(cand_stride_pages))) return 0;
   const long n_slots = static_cast<long>(cand_stride_pages) * kPage;
+  if (!uses_mean_pass(L.G(), static_cast<int>(n_slots))) return 0;
   return align_up(static_cast<size_t>(L.B) * L.Hkv * n_slots * sizeof(float), 256);
 }
 
@@ -463,14 +500,28 @@ hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* can
                        hipStream_t s) {
   const ToppArgs a{&L, weights, cand_pages, cand_count, cand_stride_pages, p, kept,
                    kept_count, tau, static_cast<float*>(stage_scratch(ws, L)), s};
-  switch (slots_per_thread(cand_stride_pages)) {
-    case 1: launch_spt<1>(a); break;
-    case 2: launch_spt<2>(a); break;
-    case 4: launch_spt<4>(a); break;
-    case 8: launch_spt<8>(a); break;
-    case 16: launch_spt<16>(a); break;
-    case 32: launch_spt<32>(a); break;
-    default: launch_spt<64>(a); break;
+  const int n_slots = cand_stride_pages * kPage;
+#if TWL_TOPP_SMALL_UNIT > 0
+  if (block_threads(n_slots) == 256) {
+    switch (slots_per_thread(n_slots)) {
+      case 1: launch_spt<256, 1>(a); break;
+      case 2: launch_spt<256, 2>(a); break;
+      case 4: launch_spt<256, 4>(a); break;
+      case 8: launch_spt<256, 8>(a); break;
+      case 16: launch_spt<256, 16>(a); break;
+      default: launch_spt<256, 32>(a); break;
+    }
+    return hipGetLastError();
+  }
+#endif
+  switch (slots_per_thread(n_slots)) {
+    case 1: launch_spt<1024, 1>(a); break;
+    case 2: launch_spt<1024, 2>(a); break;
+    case 4: launch_spt<1024, 4>(a); break;
+    case 8: launch_spt<1024, 8>(a); break;
+    case 16: launch_spt<1024, 16>(a); break;
+    case 32: launch_spt<1024, 32>(a); break;
+    default: launch_spt<1024, 64>(a); break;
   }
   return hipGetLastError();
 }

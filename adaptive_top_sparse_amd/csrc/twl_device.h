@@ -345,6 +345,63 @@ __device__ __forceinline__ uint32_t block_pick_bucket(T w0, T w1, T rem, T* lds,
   return b;
 }
 
+// Boundary bucket of a descending selection over NT * BPT buckets kept in LDS. Thread t
+// owns the contiguous buckets [t*BPT, (t+1)*BPT); bucket b is stored at
+// bins[(b % BPT) * NT + b / BPT] (see bucket_slot), so that the owners' reads are
+// conflict-free. Returns the bucket b* with weight(buckets > b*) < rem <= weight(buckets >=
+// b*); *above = weight(buckets > b*), *in = weight(b*). `lds` holds NT/64 elements, `pick`
+// 3. Requires 0 < rem <= total weight. When frac > 0, rem is replaced by
+// max(1, ceil(frac * total weight)) and *rem_used receives it, so a first pass needs no
+// separate reduction for the total.
+template <int NT, int BPT>
+__device__ __forceinline__ int bucket_slot(uint32_t b) {
+  return static_cast<int>((b % BPT) * NT + b / BPT);
+}
+
+template <int NT, int BPT, typename T>
+__device__ __forceinline__ uint32_t block_pick_bucket_lds(const T* bins, T rem, T* lds, T* pick,
+                                                          T* above, T* in, float frac = 0.f,
+                                                          T* rem_used = nullptr) {
+  constexpr int NW = NT / kWave;
+  const int t = threadIdx.x;
+  const int w = t / kWave;
+  T bv[BPT];
+  T mine = T(0);
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    bv[i] = bins[i * NT + t];
+    mine += bv[i];
+  }
+  const T incl = wave_incl_scan(mine);
+  if (lane_id() == kWave - 1) lds[w] = incl;
+  __syncthreads();
+  T x = lane_id() < NW ? lds[lane_id()] : T(0);
+  x = wave_incl_scan(x);
+  const T before = w > 0 ? readlane(x, w - 1) : T(0);
+  const T total = readlane(x, NW - 1);
+  if (frac > 0.f) {
+    rem = static_cast<T>(ceil(static_cast<double>(frac) * static_cast<double>(total)));
+    rem = rem < T(1) ? T(1) : rem;
+    if (rem_used) *rem_used = rem;
+  }
+  T abv = total - (before + incl);  // weight of the buckets above this thread's range
+#pragma unroll
+  for (int i = BPT - 1; i >= 0; --i) {
+    if (abv < rem && rem <= abv + bv[i]) {
+      pick[0] = static_cast<T>(t * BPT + i);
+      pick[1] = abv;
+      pick[2] = bv[i];
+    }
+    abv += bv[i];
+  }
+  __syncthreads();
+  const uint32_t b = static_cast<uint32_t>(pick[0]);
+  *above = pick[1];
+  *in = pick[2];
+  __syncthreads();
+  return b;
+}
+
 // ---- number formats -------------------------------------------------------------------
 
 __device__ __forceinline__ float h2f(uint16_t bits) {
