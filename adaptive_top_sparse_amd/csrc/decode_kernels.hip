@@ -7,7 +7,9 @@
 //
 // Split-KV: each work-group takes a chunk of a KV head's kept list and leaves (max, sum,
 // unnormalized o) in log2 units in the workspace; a merge kernel combines the chunks and
-// writes the fp16 output. A list that fits one chunk is finished in place. (Merging in the
+// writes the fp16 output. A list that fits one chunk is finished in place. Chunks are
+// small (one to four batches of rows), so that every row's chain of dependent loads is in
+// flight at once across the chip. (Merging in the
 // last work-group to finish, found with an atomic ticket, needs device-scope fences that
 // write back and invalidate whole L2s on this multi-XCD part; measured, it costs far more
 // than the second launch.)
@@ -34,20 +36,21 @@ namespace {
 #define TWL_DEC_UNROLL 4
 #endif
 #ifndef TWL_DEC_TARGET_BLOCKS
-#define TWL_DEC_TARGET_BLOCKS 512
+#define TWL_DEC_TARGET_BLOCKS 2048
 #endif
-#ifndef TWL_DEC_MIN_CHUNK
-#define TWL_DEC_MIN_CHUNK 64
+#ifndef TWL_DEC_MAX_BATCHES
+#define TWL_DEC_MAX_BATCHES 4
 #endif
 constexpr int kDecThreads = TWL_DEC_THREADS;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kDecUnroll = TWL_DEC_UNROLL;
-constexpr int kDecMaxChunks = 256;  // per KV head; the merge holds (m, l) of each in LDS
-#ifndef TWL_DEC_MAX_CHUNK
-#define TWL_DEC_MAX_CHUNK 512
-#endif
-constexpr int kDecMaxChunkTokens = TWL_DEC_MAX_CHUNK;  // kept tokens per work-group, at most
-constexpr int kMergeSlice = 16;     // channels per merge work-group
+constexpr int kMergeSlice = 16;  // channels per merge work-group
+
+// Kept tokens one work-group takes per batch: every wave takes kDecUnroll rows per lane
+// group, 64 / (D/8) lane groups per wave.
+__host__ __device__ constexpr int decode_batch_tokens(int d) {
+  return kDecWaves * kDecUnroll * (kWave / (d / 8));
+}
 
 __device__ __forceinline__ float rescale(float m, float M) {
   return m == -INFINITY ? 0.f : exp2f(m - M);
@@ -55,6 +58,12 @@ __device__ __forceinline__ float rescale(float m, float M) {
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
+// Each work-group takes chunk_tokens consecutive entries of a KV head's kept list, in
+// batches of decode_batch_tokens(D). A lane's rows go through three dependent loads (kept
+// id, page-table entry, K/V row), pipelined across batches: ids two batches ahead, page
+// entries one ahead. Every load is issued unconditionally (entries past the list or the
+// sequence read a valid stand-in and are masked afterwards), so no load waits behind a
+// branch; the kept count is read alongside the first ids.
 template <int D, int G>
 __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -65,11 +74,12 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     int n_chunks, int chunk_tokens, uint16_t* __restrict__ out) {
   constexpr int LPT = D / 8;        // lanes per token row
   constexpr int TPW = kWave / LPT;  // token rows per wave per load
-  constexpr int STEP = TPW * kDecUnroll;
+  constexpr int U = kDecUnroll;
+  constexpr int STEP = TPW * U;     // tokens per wave per batch
+  constexpr int BSTEP = decode_batch_tokens(D);
   constexpr int PSTRIDE = D + 4;    // floats per (chunk, head) partial: m, l, 2 pad, o[D]
   __shared__ float s_m[kDecWaves][G], s_l[kDecWaves][G];
   __shared__ float s_acc[kDecWaves][G][D];
-  __shared__ long s_row[kDecMaxChunkTokens];
   TWL_PHASE(0);
   TWL_SPAN_BEGIN();
 
@@ -78,41 +88,70 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   const int chunk = blockIdx.x;
   const long unit = static_cast<long>(b) * Hkv + g;
   const int Hq = Hkv * G;
-  int K = kept_count[unit];
-  K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
-  const int nc = (K + chunk_tokens - 1) / chunk_tokens;
   const long head0 = static_cast<long>(b) * Hq + g * G;
+  const int t0 = chunk * chunk_tokens;
+  const int tend = min(kept_stride, t0 + chunk_tokens);  // the chunk's slots in the list
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int sub = lane % LPT;
+  const int tk = lane / LPT;
+  const int c0 = sub * 8;
+  const int32_t* krow = kept + unit * kept_stride;
+  const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
+
+  // slot of this lane's row u of batch j
+  auto slot_of = [&](int j, int u) { return t0 + j * BSTEP + wave * STEP + u * TPW + tk; };
+  auto load_ids = [&](int j, int (&id)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = slot_of(j, u);
+      id[u] = krow[sl < tend ? sl : t0];
+    }
+  };
+  int ids0[U], ids1[U];
+  load_ids(0, ids0);
+  load_ids(1, ids1);
+  int K = kept_count[unit];
+  const int n = seq_len_clamped(seq_lens, b, max_pages);
+  K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
   if (K == 0) {
     // empty kept set: o = 0, written by the first work-group
     if (chunk == 0)
       for (int i = threadIdx.x; i < G * D; i += kDecThreads) out[head0 * D + i] = 0;
     return;
   }
-  const int t0 = chunk * chunk_tokens;
   if (t0 >= K) return;
   const int t1 = min(K, t0 + chunk_tokens);
-  const int n = seq_len_clamped(seq_lens, b, max_pages);
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const int sub = lane % LPT;
-  const int tk = lane / LPT;
-  const int c0 = sub * 8;
+  const int nc = (K + chunk_tokens - 1) / chunk_tokens;
+  const int n_batches = (t1 - t0 + BSTEP - 1) / BSTEP;
 
-  // the chunk's kept ids -> element offsets of their cache rows (-1: absent), once
-  {
-    const int32_t* krow = kept + unit * kept_stride;
-    const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
-    for (int i = threadIdx.x; i < t1 - t0; i += kDecThreads) {
-      const int tok = krow[t0 + i];
-      long row = -1;
-      if (tok >= 0 && tok < n) {
-        const int phys = trow[tok / kPage];
-        if (phys_ok(phys, num_phys))
-          row = ((static_cast<long>(phys) * Hkv + g) * kPage + tok % kPage) * D;
-      }
-      s_row[i] = row;
+  // page entries of batch j: the token's page id (or a stand-in) and its in-page offset
+  auto load_rows = [&](int j, const int (&id)[U], int (&phys)[U], int (&tok)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = slot_of(j, u);
+      const int t = id[u];
+      const bool ok = sl < t1 && t >= 0 && t < n;
+      tok[u] = ok ? t : -1;
+      phys[u] = trow[ok ? t / kPage : 0];
     }
-  }
+  };
+  auto row_of = [&](int phys, int tok) -> long {
+    if (tok < 0 || !phys_ok(phys, num_phys)) return -1;
+    return ((static_cast<long>(phys) * Hkv + g) * kPage + tok % kPage) * D;
+  };
+  auto load_kv = [&](const int (&phys)[U], const int (&tok)[U], bool (&live)[U],
+                     u32x4 (&kv)[U], u32x4 (&vv)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long row = row_of(phys[u], tok[u]);
+      live[u] = row >= 0;
+      const long r = row >= 0 ? row : 0;
+      kv[u] = *reinterpret_cast<const u32x4*>(k_cache + r + c0);
+      vv[u] = *reinterpret_cast<const u32x4*>(v_cache + r + c0);
+    }
+  };
+
   uint32_t qw[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -128,63 +167,50 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
   }
-  __syncthreads();
 
-  // this wave's batches: token slots base + u*TPW + tk, base stepping by all waves' batches
-  const int n_tok = t1 - t0;
-  auto load_batch = [&](int base, long (&row)[kDecUnroll], u32x4 (&kv)[kDecUnroll],
-                        u32x4 (&vv)[kDecUnroll]) {
-#pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      const int t = base + u * TPW + tk;
-      row[u] = t < n_tok ? s_row[t] : -1;
-      if (row[u] >= 0) {
-        kv[u] = *reinterpret_cast<const u32x4*>(k_cache + row[u] + c0);
-        vv[u] = *reinterpret_cast<const u32x4*>(v_cache + row[u] + c0);
-      } else {
-        kv[u] = u32x4{0u, 0u, 0u, 0u};
-        vv[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  long row[kDecUnroll];
-  u32x4 kv[kDecUnroll], vv[kDecUnroll];
-  int base = wave * STEP;
-  if (base < n_tok) load_batch(base, row, kv, vv);
-  for (; base < n_tok; base += kDecWaves * STEP) {
-    // prefetch the next batch before computing this one
-    long row_n[kDecUnroll];
-    u32x4 kv_n[kDecUnroll], vv_n[kDecUnroll];
-    const int next = base + kDecWaves * STEP;
-    if (next < n_tok) load_batch(next, row_n, kv_n, vv_n);
+  // pipeline: rows of batch 0, K/V of batch 0, rows of batch 1
+  int phys0[U], tok0[U], phys1[U], tok1[U];
+  load_rows(0, ids0, phys0, tok0);
+  bool live0[U];
+  u32x4 kv0[U], vv0[U];
+  load_kv(phys0, tok0, live0, kv0, vv0);
+  if (n_batches > 1) load_rows(1, ids1, phys1, tok1);
 
-    float s[kDecUnroll][G];
+  for (int j = 0; j < n_batches; ++j) {
+    // ids of batch j + 2 and K/V of batch j + 1 go out before batch j is used
+    int ids2[U];
+    if (j + 2 < n_batches) load_ids(j + 2, ids2);
+    bool live1[U];
+    u32x4 kv1[U], vv1[U];
+    if (j + 1 < n_batches) load_kv(phys1, tok1, live1, kv1, vv1);
+
+    float s[U][G];
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          d = __builtin_amdgcn_fdot2(as_h2(qw[h][j]), as_h2(kv[u][j]), d, false);
+        for (int jj = 0; jj < 4; ++jj)
+          d = __builtin_amdgcn_fdot2(as_h2(qw[h][jj]), as_h2(kv0[u][jj]), d, false);
         d = group_sum<LPT>(d);
-        s[u][h] = row[u] >= 0 ? d * scale_log2 : -INFINITY;
+        s[u][h] = live0[u] ? d * scale_log2 : -INFINITY;
       }
     }
     // one running max per head for the whole wave: the token groups' batch maxima are
     // combined across groups, so every group's (l, acc) stays on the same scale
-    float pr[kDecUnroll][G];
+    float pr[U][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mb = s[0][h];
 #pragma unroll
-      for (int u = 1; u < kDecUnroll; ++u) mb = fmaxf(mb, s[u][h]);
+      for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
       mb = across_groups<LPT>(mb, OpMax());
       const float mn = fmaxf(m[h], mb);
       const float alpha = rescale(m[h], mn);
       float lsum = l[h] * alpha;
 #pragma unroll
-      for (int u = 0; u < kDecUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         pr[u][h] = mn == -INFINITY ? 0.f : rescale(s[u][h], mn);
         lsum += pr[u][h];
       }
@@ -194,13 +220,13 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       m[h] = mn;
     }
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       float vf[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f16x2 p2 = as_h2(vv[u][j]);
-        vf[2 * j] = static_cast<float>(p2[0]);
-        vf[2 * j + 1] = static_cast<float>(p2[1]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const f16x2 p2 = as_h2(vv0[u][jj]);
+        vf[2 * jj] = static_cast<float>(p2[0]);
+        vf[2 * jj + 1] = static_cast<float>(p2[1]);
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -208,14 +234,23 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
         for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(pr[u][h], vf[c], acc[h][c]);
       }
     }
+    // rotate the pipeline
+    if (j + 2 < n_batches) {
+      int phys2[U], tok2[U];
+      load_rows(j + 2, ids2, phys2, tok2);
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      row[u] = row_n[u];
-      kv[u] = kv_n[u];
-      vv[u] = vv_n[u];
+      for (int u = 0; u < U; ++u) {
+        phys1[u] = phys2[u];
+        tok1[u] = tok2[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      live0[u] = live1[u];
+      kv0[u] = kv1[u];
+      vv0[u] = vv1[u];
     }
   }
-
   TWL_PHASE(1);
   // sum the token groups of each channel slice (same scale: m is shared by the wave)
 #pragma unroll
@@ -224,42 +259,72 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = across_groups<LPT>(acc[h][c], OpSum());
   }
-  if (tk == 0) {
+  if constexpr (kDecWaves == 1) {
+    // one wave per work-group: lanes of token group 0 hold the chunk's totals
+    if (tk == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (sub == 0) {
-        s_m[wave][h] = m[h];
-        s_l[wave][h] = l[h];
+      for (int h = 0; h < G; ++h) {
+        if (nc == 1) {
+          const float L = l[h];
+          u32x4 o;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f16x2 pr2 = {static_cast<f16>(L > 0.f ? acc[h][2 * jj] / L : 0.f),
+                               static_cast<f16>(L > 0.f ? acc[h][2 * jj + 1] / L : 0.f)};
+            o[jj] = __builtin_bit_cast(uint32_t, pr2);
+          }
+          *reinterpret_cast<u32x4*>(out + (head0 + h) * D + c0) = o;
+        } else {
+          float* dst = partials + ((head0 + h) * n_chunks + chunk) * PSTRIDE;
+          if (sub == 0) {
+            dst[0] = m[h];
+            dst[1] = l[h];
+          }
+          *reinterpret_cast<f32x4*>(dst + 4 + c0) =
+              f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+          *reinterpret_cast<f32x4*>(dst + 8 + c0) =
+              f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+        }
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s_acc[wave][h][c0 + c] = acc[h][c];
     }
-  }
-  __syncthreads();
-  TWL_PHASE(2);
-  // this chunk's (M, L, A) per head, merged over the waves
-  for (int i = threadIdx.x; i < G * D; i += kDecThreads) {
-    const int h = i / D, c = i % D;
-    float M = s_m[0][h];
+  } else {
+    if (tk == 0) {
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, A = 0.f;
+      for (int h = 0; h < G; ++h) {
+        if (sub == 0) {
+          s_m[wave][h] = m[h];
+          s_l[wave][h] = l[h];
+        }
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float f = rescale(s_m[w][h], M);
-      L += s_l[w][h] * f;
-      A += s_acc[w][h][c] * f;
-    }
-    if (nc == 1) {
-      const float o = L > 0.f ? A / L : 0.f;
-      out[(head0 + h) * D + c] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
-    } else {
-      float* dst = partials + ((head0 + h) * n_chunks + chunk) * PSTRIDE;
-      if (c == 0) {
-        dst[0] = M;
-        dst[1] = L;
+        for (int c = 0; c < 8; ++c) s_acc[wave][h][c0 + c] = acc[h][c];
       }
-      dst[4 + c] = A;
+    }
+    __syncthreads();
+    TWL_PHASE(2);
+    // this chunk's (M, L, A) per head, merged over the waves
+    for (int i = threadIdx.x; i < G * D; i += kDecThreads) {
+      const int h = i / D, c = i % D;
+      float M = s_m[0][h];
+#pragma unroll
+      for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float f = rescale(s_m[w][h], M);
+        L += s_l[w][h] * f;
+        A += s_acc[w][h][c] * f;
+      }
+      if (nc == 1) {
+        const float o = L > 0.f ? A / L : 0.f;
+        out[(head0 + h) * D + c] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
+      } else {
+        float* dst = partials + ((head0 + h) * n_chunks + chunk) * PSTRIDE;
+        if (c == 0) {
+          dst[0] = M;
+          dst[1] = L;
+        }
+        dst[4 + c] = A;
+      }
     }
   }
   TWL_PHASE(3);
@@ -267,14 +332,13 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 }
 
 // Merge of the chunk partials when they are more than one: one wave per (sequence, query
-// head, 16-channel slice). Lanes take chunks; every load is independent, so the whole merge
-// is about two memory round trips.
+// head, 16-channel slice). Lane i takes chunks i, i + 64, ... with a running (max, sum, o)
+// of its own; the lanes are then combined on the common maximum.
 template <int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     const float* __restrict__ partials, const int32_t* __restrict__ kept_count, int kept_stride,
     int Hkv, int G, int n_chunks, int chunk_tokens, uint16_t* __restrict__ out) {
   constexpr int PSTRIDE = D + 4;
-  constexpr int PER = kDecMaxChunks / kWave;  // chunks per lane at most
   __shared__ float s_acc[kWave][kMergeSlice + 1];
   const int slice = blockIdx.x;
   const int h = blockIdx.y;
@@ -287,45 +351,32 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
   if (nc <= 1) return;  // finished by the partial kernel
   const int lane = lane_id();
   const float* ph = partials + (static_cast<long>(b) * Hq + h) * n_chunks * PSTRIDE;
-  float mi[PER], li[PER];
-  f32x4 a[PER][kMergeSlice / 4];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int i = lane + k * kWave;
-    const bool ok = i < nc;
-    const float* pi = ph + static_cast<long>(i) * PSTRIDE;
-    mi[k] = ok ? pi[0] : -INFINITY;
-    li[k] = ok ? pi[1] : 0.f;
-#pragma unroll
-    for (int v = 0; v < kMergeSlice / 4; ++v) {
-      if (ok) {
-        a[k][v] = *reinterpret_cast<const f32x4*>(pi + 4 + slice * kMergeSlice + 4 * v);
-      } else {
-        a[k][v] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  }
-  float M = mi[0];
-#pragma unroll
-  for (int k = 1; k < PER; ++k) M = fmaxf(M, mi[k]);
-  M = wave_max(M);
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float acc[kMergeSlice];
 #pragma unroll
   for (int c = 0; c < kMergeSlice; ++c) acc[c] = 0.f;
+  for (int i = lane; i < nc; i += kWave) {
+    const float* pi = ph + static_cast<long>(i) * PSTRIDE;
+    const float mi = pi[0], li = pi[1];
+    f32x4 a[kMergeSlice / 4];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const float f = rescale(mi[k], M);
-    L = fmaf(li[k], f, L);
+    for (int v = 0; v < kMergeSlice / 4; ++v)
+      a[v] = *reinterpret_cast<const f32x4*>(pi + 4 + slice * kMergeSlice + 4 * v);
+    const float Mn = fmaxf(M, mi);
+    const float fo = rescale(M, Mn), fi = rescale(mi, Mn);
+    L = L * fo + li * fi;
 #pragma unroll
     for (int v = 0; v < kMergeSlice / 4; ++v) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[4 * v + j] = fmaf(a[k][v][j], f, acc[4 * v + j]);
+      for (int j = 0; j < 4; ++j) acc[4 * v + j] = acc[4 * v + j] * fo + a[v][j] * fi;
     }
+    M = Mn;
   }
-  L = wave_sum(L);
+  const float Mw = wave_max(M);
+  const float f = rescale(M, Mw);
+  L = wave_sum(L * f);
 #pragma unroll
-  for (int c = 0; c < kMergeSlice; ++c) s_acc[lane][c] = acc[c];
+  for (int c = 0; c < kMergeSlice; ++c) s_acc[lane][c] = acc[c] * f;
   __syncthreads();
   if (lane < kMergeSlice) {
     float t = 0.f;
@@ -364,15 +415,14 @@ void decode_dispatch_g(const Layout& L, const void* q, const void* k, const void
 }  // namespace
 
 int decode_chunk_tokens(const Layout& L, int kept_stride) {
-  // about TWL_DEC_TARGET_BLOCKS work-groups over the largest possible kept lists, at most
-  // kDecMaxChunks chunks per KV head, at most kDecMaxChunkTokens tokens per chunk
+  // about TWL_DEC_TARGET_BLOCKS work-groups over the largest possible kept lists: one to
+  // TWL_DEC_MAX_BATCHES batches per work-group
   const long units = static_cast<long>(L.B) * L.Hkv;
-  const long by_blocks =
+  const long want =
       (static_cast<long>(kept_stride) * units + TWL_DEC_TARGET_BLOCKS - 1) / TWL_DEC_TARGET_BLOCKS;
-  const long by_merge = (static_cast<long>(kept_stride) + kDecMaxChunks - 1) / kDecMaxChunks;
-  const long want = by_blocks > by_merge ? by_blocks : by_merge;
-  long c = TWL_DEC_MIN_CHUNK;
-  while (c < want && c < kDecMaxChunkTokens) c <<= 1;
+  const int batch = decode_batch_tokens(L.d);
+  long c = batch;
+  while (c < want && c < static_cast<long>(batch) * TWL_DEC_MAX_BATCHES) c <<= 1;
   return static_cast<int>(c);
 }
 

@@ -16,8 +16,36 @@ TWL_PHASE_STORAGE(estimate)
 namespace twl {
 namespace {
 
-// One lane per candidate slot, kEstChunk slots per block. The query group (G x D) and its
-// per-group sums sit in LDS as fp32 and are read as broadcasts.
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kEstWaves = kEstChunk / kWave;             // 4
+constexpr int kPagesPerWave = kEstChunk / kPage / kEstWaves;  // candidate pages per wave
+
+// The per-group dot products on the matrix cores: one v_mfma_f32_16x16x16_f16 takes a
+// 16-token tile (one candidate page) and 16 channels of a 32-channel group, with
+//   A = the group's query heads (rows, padded to 16 with zeros) x channels,
+//   B = channels x the tile's tokens (the 4-bit codes as exact fp16 integers),
+// and leaves D[head][token] in fp32: lane l holds heads 4(l/16)..+3 of token l%16. Lane l
+// feeds channel slots 4(l/16)..+3, which are permuted so that the codes unpack cheaply:
+// lane group c4 = l/16 covers channels 8 c4 .. 8 c4 + 7 of the group (one 32-bit word of
+// codes), slot order {0,4,1,5} in the first and {2,6,3,7} in the second instruction. A dot
+// product is invariant to a common permutation of both operands, and every product of an
+// fp16 q and a code is exact in fp32.
+__device__ __forceinline__ int mfma_channel(int c4, int m, int e) {
+  constexpr int kPerm[2][4] = {{0, 4, 1, 5}, {2, 6, 3, 7}};
+  return 8 * c4 + kPerm[m][e];
+}
+
+// Two fp16 codes from the nibble pair at bits [3:0] and [19:16]: 1024 + n is exact in fp16
+// (its ulp is 1), so or-ing n into the significand of 1024 and subtracting 1024 gives n.
+__device__ __forceinline__ uint32_t codes_to_f16x2(uint32_t pair_bits) {
+  const f16x2 v = __builtin_bit_cast(f16x2, pair_bits | 0x64006400u);
+  const f16x2 r = v - f16x2{static_cast<f16>(1024.f), static_cast<f16>(1024.f)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// One block per kEstChunk candidate slots (16 pages) of a (sequence, KV head); wave w takes
+// pages 4w..4w+3 of the chunk, one MFMA tile each.
 template <int D, int G>
 __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
@@ -27,132 +55,185 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     int num_phys, float sm_scale, float* __restrict__ logits, float2* __restrict__ partials,
     int n_chunks) {
   constexpr int NG = D / 32;
-  constexpr int Hq_per = G;
-  __shared__ float qs[G][D];
+  constexpr int HR = G < 4 ? G : 4;  // heads per lane (rows 4(l/16)..+3 that exist)
+  static_assert(G <= 8, "at most 8 query heads per KV head");
+  __shared__ f16 qs[G][D];
   __shared__ float qsum[G][NG];
+  __shared__ float red_m[kEstWaves][G], red_l[kEstWaves][G];
   TWL_PHASE(0);
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int chunk = blockIdx.x;
   const int Hq = Hkv * G;
   const long unit = static_cast<long>(b) * Hkv + g;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int tok_in_page = lane % 16;
+  const int c4 = lane / 16;
+  const int n = seq_len_clamped(seq_lens, b, max_pages);
+  const int n_slots = cand_stride_pages * kPage;
 
+  // this wave's pages: candidate rank -> page id -> physical page (wave-uniform loads; the
+  // page ids are read before the candidate count is known, from inside the row)
+  int rank[kPagesPerWave], pid[kPagesPerWave], phys[kPagesPerWave];
+#pragma unroll
+  for (int i = 0; i < kPagesPerWave; ++i) {
+    rank[i] = (chunk * kEstWaves + wave) * kPagesPerWave + i;
+    if (cand_pages == nullptr) {
+      pid[i] = rank[i];
+    } else {
+      const int r = rank[i] < cand_stride_pages ? rank[i] : 0;
+      pid[i] = cand_pages[unit * cand_stride_pages + r];
+    }
+  }
+  int cnt = cand_stride_pages;
+  if (cand_pages != nullptr) {
+    cnt = cand_count ? cand_count[unit] : (n + kPage - 1) / kPage;
+    cnt = cnt < cand_stride_pages ? cnt : cand_stride_pages;
+  }
+#pragma unroll
+  for (int i = 0; i < kPagesPerWave; ++i) {
+    const bool ok = rank[i] < cnt && pid[i] >= 0 && pid[i] < max_pages && pid[i] * kPage < n;
+    pid[i] = ok ? pid[i] : -1;
+    phys[i] = page_table[static_cast<long>(b) * max_pages + (ok ? pid[i] : 0)];
+  }
+  // codes (one word per group) and {scale, zero} of this lane's token in each page
+  uint32_t cw[kPagesPerWave][NG], mw[kPagesPerWave][NG];
+#pragma unroll
+  for (int i = 0; i < kPagesPerWave; ++i) {
+    const bool ok = pid[i] >= 0 && phys_ok(phys[i], num_phys);
+    const long row = ok ? (static_cast<long>(phys[i]) * Hkv + g) * kPage + tok_in_page : 0;
+    const uint32_t* crow = reinterpret_cast<const uint32_t*>(codes + row * (D / 2));
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp) {
+      cw[i][grp] = crow[grp * 4 + c4];
+      mw[i][grp] = meta[row * NG + grp];
+    }
+    if (!ok) pid[i] = -1;
+  }
+
+  // the group's queries and their per-group sums
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int h = i / D, c = i % D;
-    qs[h][c] = h2f(q[(static_cast<long>(b) * Hq + g * Hq_per + h) * D + c]);
+    qs[h][c] = __builtin_bit_cast(f16, q[(static_cast<long>(b) * Hq + g * G + h) * D + c]);
   }
   __syncthreads();
   if (threadIdx.x < G * NG) {
     const int h = threadIdx.x / NG, grp = threadIdx.x % NG;
     float acc = 0.f;
-    for (int c = 0; c < 32; ++c) acc += qs[h][grp * 32 + c];
+    for (int c = 0; c < 32; ++c) acc += static_cast<float>(qs[h][grp * 32 + c]);
     qsum[h][grp] = acc;
   }
   __syncthreads();
-
-  const int n = seq_len_clamped(seq_lens, b, max_pages);
-  const int n_slots = cand_stride_pages * kPage;
-  const int slot = chunk * kEstChunk + threadIdx.x;
-  int tok = -1;
-  if (slot < n_slots) {
-    if (cand_pages == nullptr) {
-      tok = slot;
-    } else {
-      int cnt = cand_count ? cand_count[unit] : (n + kPage - 1) / kPage;
-      cnt = cnt < cand_stride_pages ? cnt : cand_stride_pages;
-      const int r = slot / kPage;
-      if (r < cnt) {
-        const int pg = cand_pages[unit * cand_stride_pages + r];
-        tok = pg >= 0 ? pg * kPage + slot % kPage : -1;
-      }
+  // A operands: row = head lane%16 (zero past G), channel slots as in mfma_channel
+  f16x4 qa[NG][2];
+  const int qh = lane % 16;
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qa[grp][m][e] = qh < G ? qs[qh < G ? qh : 0][grp * 32 + mfma_channel(c4, m, e)]
+                               : static_cast<f16>(0.f);
+  float qg[NG][HR];  // Q_grp of this lane's output heads 4 c4 + r
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+    for (int r = 0; r < HR; ++r) {
+      const int h = 4 * c4 + r;
+      qg[grp][r] = h < G ? qsum[h < G ? h : 0][grp] : 0.f;
     }
-  }
   TWL_PHASE(1);
-  bool valid = tok >= 0 && tok < n;
-  float s[G];
+
+  const int wave_slot0 = (chunk * kEstWaves + wave) * kPagesPerWave * kPage;
+  float s[kPagesPerWave][HR];
 #pragma unroll
-  for (int h = 0; h < G; ++h) s[h] = -INFINITY;
-  if (valid) {
-    const int phys = page_table[static_cast<long>(b) * max_pages + tok / kPage];
-    valid = phys_ok(phys, num_phys);
-    if (valid) {
-      const long row = (static_cast<long>(phys) * Hkv + g) * kPage + tok % kPage;
-      const u32x4* crow = reinterpret_cast<const u32x4*>(codes + row * (D / 2));
-      u32x4 cw[NG];
+  for (int i = 0; i < kPagesPerWave; ++i) {
+    float acc[HR];
 #pragma unroll
-      for (int grp = 0; grp < NG; ++grp) cw[grp] = crow[grp];
-      uint32_t mw[NG];
+    for (int r = 0; r < HR; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int grp = 0; grp < NG; ++grp) mw[grp] = meta[row * NG + grp];
-      float acc[G];
+    for (int grp = 0; grp < NG; ++grp) {
+      const uint32_t w = cw[i][grp];
+      uint32_t bw[4];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = 0.f;
+      for (int k = 0; k < 4; ++k) bw[k] = codes_to_f16x2((w >> (4 * k)) & 0x000f000fu);
+      const f16x4 b0 = __builtin_bit_cast(f16x4, u32x2{bw[0], bw[1]});
+      const f16x4 b1 = __builtin_bit_cast(f16x4, u32x2{bw[2], bw[3]});
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      d = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[grp][0], b0, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[grp][1], b1, d, 0, 0, 0);
+      const float scale = h2f(static_cast<uint16_t>(mw[i][grp] & 0xffffu));
+      const float zero = h2f(static_cast<uint16_t>(mw[i][grp] >> 16));
 #pragma unroll
-      for (int grp = 0; grp < NG; ++grp) {
-        float dot[G];
+      for (int r = 0; r < HR; ++r) acc[r] = fmaf(scale, d[r], fmaf(zero, qg[grp][r], acc[r]));
+    }
+    const int t = pid[i] * kPage + tok_in_page;
+    const bool valid = pid[i] >= 0 && t < n;
 #pragma unroll
-        for (int h = 0; h < G; ++h) dot[h] = 0.f;
+    for (int r = 0; r < HR; ++r) s[i][r] = valid ? sm_scale * acc[r] : -INFINITY;
+  }
+  TWL_PHASE(2);
+  // logits rows, then (max, sum exp) of this chunk per head
+  const bool head_lane = 4 * c4 < G;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t word = cw[grp][w];
-          const uint32_t lo = word & 0x0f0f0f0fu;         // channels 0,2,4,6 of the word
-          const uint32_t hi = (word >> 4) & 0x0f0f0f0fu;  // channels 1,3,5,7
-          float cv[8];
+  for (int i = 0; i < kPagesPerWave; ++i) {
+    const int slot = wave_slot0 + i * kPage + tok_in_page;
+    if (head_lane && slot < n_slots) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            cv[2 * j] = static_cast<float>((lo >> (8 * j)) & 0xffu);
-            cv[2 * j + 1] = static_cast<float>((hi >> (8 * j)) & 0xffu);
-          }
-          const int cbase = grp * 32 + w * 8;
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dot[h] = fmaf(qs[h][cbase + j], cv[j], dot[h]);
-          }
-        }
-        const float scale = h2f(static_cast<uint16_t>(mw[grp] & 0xffffu));
-        const float zero = h2f(static_cast<uint16_t>(mw[grp] >> 16));
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = fmaf(scale, dot[h], fmaf(zero, qsum[h][grp], acc[h]));
+      for (int r = 0; r < HR; ++r) {
+        const int h = 4 * c4 + r;
+        if (h < G) logits[(static_cast<long>(b) * Hq + g * G + h) * n_slots + slot] = s[i][r];
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = sm_scale * acc[h];
     }
   }
-  // logits row, then (max, sum exp) of this chunk per head: one max pass and one sum pass
-  // for all G heads
-  __shared__ float red_m[kEstChunk / kWave][G], red_l[kEstChunk / kWave][G];
-  const int wave = threadIdx.x / kWave;
-  TWL_PHASE(2);
+  // per head: max over this wave's 64 slots (4 pages in registers, 16 tokens across the row)
+  float wm[HR];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const long hrow = static_cast<long>(b) * Hq + g * G + h;
-    if (slot < n_slots) logits[hrow * n_slots + slot] = s[h];
-    const float wm = wave_max(s[h]);
-    if (lane_id() == 0) red_m[wave][h] = wm;
+  for (int r = 0; r < HR; ++r) {
+    float v = s[0][r];
+#pragma unroll
+    for (int i = 1; i < kPagesPerWave; ++i) v = fmaxf(v, s[i][r]);
+    wm[r] = group_reduce<16>(v, OpMax());
+  }
+  if (head_lane && tok_in_page == 0) {
+#pragma unroll
+    for (int r = 0; r < HR; ++r)
+      if (4 * c4 + r < G) red_m[wave][4 * c4 + r] = wm[r];
   }
   __syncthreads();
-  float e[G];
+  float e_sum[HR];
+  float M[HR];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int r = 0; r < HR; ++r) {
+    const int h = 4 * c4 + r < G ? 4 * c4 + r : 0;
     float m = red_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kEstChunk / kWave; ++w) m = fmaxf(m, red_m[w][h]);
-    e[h] = (valid && m > -INFINITY) ? expf(s[h] - m) : 0.f;
-    const float ws = wave_sum(e[h]);
-    if (lane_id() == 0) red_l[wave][h] = ws;
+    for (int w2 = 1; w2 < kEstWaves; ++w2) m = fmaxf(m, red_m[w2][h]);
+    M[r] = m;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPagesPerWave; ++i)
+      acc += (s[i][r] > -INFINITY && m > -INFINITY) ? expf(s[i][r] - m) : 0.f;
+    e_sum[r] = group_reduce<16>(acc, OpSum());
+  }
+  if (head_lane && tok_in_page == 0) {
+#pragma unroll
+    for (int r = 0; r < HR; ++r)
+      if (4 * c4 + r < G) red_l[wave][4 * c4 + r] = e_sum[r];
   }
   __syncthreads();
   if (threadIdx.x < G) {
     const int h = threadIdx.x;
     float m = red_m[0][h], l = 0.f;
 #pragma unroll
-    for (int w = 1; w < kEstChunk / kWave; ++w) m = fmaxf(m, red_m[w][h]);
+    for (int w2 = 1; w2 < kEstWaves; ++w2) m = fmaxf(m, red_m[w2][h]);
 #pragma unroll
-    for (int w = 0; w < kEstChunk / kWave; ++w) l += red_l[w][h];
-    const long hrow = static_cast<long>(b) * Hq + g * G + h;
-    partials[hrow * n_chunks + chunk] = make_float2(m, l);
+    for (int w2 = 0; w2 < kEstWaves; ++w2) l += red_l[w2][h];
+    partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(m, l);
   }
+  (void)M;
   TWL_PHASE(3);
 }
 

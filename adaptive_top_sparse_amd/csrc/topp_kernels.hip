@@ -174,7 +174,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     float* __restrict__ tau_out) {
   using M = SlotMap<NT, SPT>;
   using S = ToppShape<NT>;
-  constexpr int VW = M::VW, NV = M::NV, NR = M::NR, NL = M::NL;
+  constexpr int VW = M::VW, NR = M::NR, NL = M::NL;
   constexpr int NW = S::kWaves, BPT = S::kBpt;
   static_assert(NL == 0 || VW == 4, "LDS-resident vectors are four wide");
   // the mass histogram, bucket b at bucket_slot<NT, BPT>(b); after a pass has picked its

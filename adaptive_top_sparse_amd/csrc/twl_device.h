@@ -175,6 +175,18 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Reduction with `op` over aligned groups of W lanes (W in {2, 4, 8, 16}); every lane of a
+// group ends with the group's result.
+template <int W, typename Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group width");
+  v = op(v, dpp_f32<kQuadXor1>(v));
+  if constexpr (W >= 4) v = op(v, dpp_f32<kQuadXor2>(v));
+  if constexpr (W >= 8) v = op(v, dpp_f32<kRowHalfMirror>(v));
+  if constexpr (W >= 16) v = op(v, dpp_f32<kRowMirror>(v));
+  return v;
+}
+
 // Combine the lanes that hold the same position within their W-lane group, over all
 // 64 / W groups of the wave (W in {8, 16}); every lane ends with the combined value. Uses
 // a DPP rotate inside rows and the gfx950 permlane swaps across rows.
