@@ -18,22 +18,36 @@ namespace {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kEstWaves = kEstChunk / kWave;             // 4
-constexpr int kPagesPerWave = kEstChunk / kPage / kEstWaves;  // candidate pages per wave
+constexpr int kEstWaves = kEstChunk / kWave;  // 4
+constexpr int kEstBatch = 4;                  // candidate pages per wave per batch
+constexpr int kNormThreads = 256;
+constexpr int kNormSlots = kNormThreads * 16;  // weights per normalization work-group
+#ifndef TWL_EST_TARGET_BLOCKS
+#define TWL_EST_TARGET_BLOCKS 1024
+#endif
+#ifndef TWL_EST_MAX_CHUNK_PAGES
+#define TWL_EST_MAX_CHUNK_PAGES 256
+#endif
 
-// The per-group dot products on the matrix cores: one v_mfma_f32_16x16x16_f16 takes a
-// 16-token tile (one candidate page) and 16 channels of a 32-channel group, with
-//   A = the group's query heads (rows, padded to 16 with zeros) x channels,
-//   B = channels x the tile's tokens (the 4-bit codes as exact fp16 integers),
-// and leaves D[head][token] in fp32: lane l holds heads 4(l/16)..+3 of token l%16. Lane l
-// feeds channel slots 4(l/16)..+3, which are permuted so that the codes unpack cheaply:
-// lane group c4 = l/16 covers channels 8 c4 .. 8 c4 + 7 of the group (one 32-bit word of
-// codes), slot order {0,4,1,5} in the first and {2,6,3,7} in the second instruction. A dot
-// product is invariant to a common permutation of both operands, and every product of an
-// fp16 q and a code is exact in fp32.
-__device__ __forceinline__ int mfma_channel(int c4, int m, int e) {
+// The dot products run on the matrix cores, one 16-token tile (a candidate page) at a time,
+// with v_mfma_f32_16x16x16_f16 (lane l supplies A[l%16][4(l/16)..+3] and
+// B[4(l/16)..+3][l%16] and receives D[4(l/16)..+3][l%16]):
+//  * B = channels x tokens: the 4-bit codes as exact fp16 integers. Lane group c4 = l/16
+//    supplies "virtual group" c4, the c4-th quarter of the channels (D/4 of them, one
+//    contiguous run of the token's code row), four channels per instruction.
+//  * A = rows (c4, h) = virtual group x query head, block-diagonal: row (c4, h) carries
+//    q_h on the channels of virtual group c4 and 0 elsewhere.
+//  * Over the D/16 instructions D[(c4, h)][t] accumulates the dot product of q_h with the
+//    codes of virtual group c4 of token t, for up to 4 heads (a second set of instructions
+//    covers heads 4..7).
+// Lane (t, c4) scales its group's dot products (scale, plus zero * Q_grp once per real
+// group), the four lane groups' terms are summed across rows, and lane (t, c4) keeps head
+// c4 (and c4 + 4). A dot product is invariant to a common permutation of both operands, so
+// the channel slots are ordered for cheap unpacking ({0,4,1,5} then {2,6,3,7} within each
+// 8-channel word); every product of an fp16 q and a code is exact in fp32.
+__device__ __forceinline__ int mfma_channel(int c4, int vg_channels, int m, int e) {
   constexpr int kPerm[2][4] = {{0, 4, 1, 5}, {2, 6, 3, 7}};
-  return 8 * c4 + kPerm[m][e];
+  return c4 * vg_channels + 8 * (m / 2) + kPerm[m % 2][e];
 }
 
 // Two fp16 codes from the nibble pair at bits [3:0] and [19:16]: 1024 + n is exact in fp16
@@ -44,8 +58,32 @@ __device__ __forceinline__ uint32_t codes_to_f16x2(uint32_t pair_bits) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// One block per kEstChunk candidate slots (16 pages) of a (sequence, KV head); wave w takes
-// pages 4w..4w+3 of the chunk, one MFMA tile each.
+template <int NG>
+struct CodeWords {
+  uint32_t w[NG];
+};
+template <int NG>
+__device__ __forceinline__ CodeWords<NG> load_words(const uint32_t* p) {
+  CodeWords<NG> r;
+  if constexpr (NG == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    r.w[0] = v[0];
+    r.w[1] = v[1];
+    r.w[2] = v[2];
+    r.w[3] = v[3];
+  } else {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    r.w[0] = v[0];
+    r.w[1] = v[1];
+  }
+  return r;
+}
+
+// One block per chunk of chunk_pages candidate pages of a (sequence, KV head). Wave w takes
+// batches of kEstBatch pages (pages (j * 4 + w) * kEstBatch .. of the chunk, batch j), one
+// MFMA tile per page. Each page goes through three dependent loads (candidate page id, page
+// table, codes and metadata), pipelined across batches: ids two batches ahead, page-table
+// entries and codes one ahead. The chunk's (max, sum exp) per head is kept online per lane.
 template <int D, int G>
 __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
@@ -53,9 +91,12 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages, int Hkv, int max_pages,
     int num_phys, float sm_scale, float* __restrict__ logits, float2* __restrict__ partials,
-    int n_chunks) {
+    int chunk_pages, int n_chunks) {
   constexpr int NG = D / 32;
-  constexpr int HR = G < 4 ? G : 4;  // heads per lane (rows 4(l/16)..+3 that exist)
+  constexpr int VG = D / 4;           // channels per virtual group (lane group)
+  constexpr int MPT = D / 16;         // instructions per tile and head set
+  constexpr int NHB = (G + 3) / 4;    // head sets of up to 4 heads
+  constexpr int PB = kEstBatch;
   static_assert(G <= 8, "at most 8 query heads per KV head");
   __shared__ f16 qs[G][D];
   __shared__ float qsum[G][NG];
@@ -72,45 +113,58 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   const int c4 = lane / 16;
   const int n = seq_len_clamped(seq_lens, b, max_pages);
   const int n_slots = cand_stride_pages * kPage;
+  const int page0 = chunk * chunk_pages;
+  const int page_end = min(cand_stride_pages, page0 + chunk_pages);
+  const int n_batches = (page_end - page0 + kEstWaves * PB - 1) / (kEstWaves * PB);
+  const int32_t* crow = cand_pages ? cand_pages + unit * cand_stride_pages : nullptr;
 
-  // this wave's pages: candidate rank -> page id -> physical page (wave-uniform loads; the
-  // page ids are read before the candidate count is known, from inside the row)
-  int rank[kPagesPerWave], pid[kPagesPerWave], phys[kPagesPerWave];
+  auto rank_of = [&](int j, int i) { return page0 + (j * kEstWaves + wave) * PB + i; };
+  // page ids of batch j, read before the candidate count is known (from inside the row)
+  auto load_ids = [&](int j, int (&pid)[PB]) {
 #pragma unroll
-  for (int i = 0; i < kPagesPerWave; ++i) {
-    rank[i] = (chunk * kEstWaves + wave) * kPagesPerWave + i;
-    if (cand_pages == nullptr) {
-      pid[i] = rank[i];
-    } else {
-      const int r = rank[i] < cand_stride_pages ? rank[i] : 0;
-      pid[i] = cand_pages[unit * cand_stride_pages + r];
+    for (int i = 0; i < PB; ++i) {
+      const int r = rank_of(j, i);
+      pid[i] = crow == nullptr ? r : crow[r < page_end ? r : page0];
     }
-  }
+  };
+  int ids0[PB], ids1[PB];
+  load_ids(0, ids0);
+  load_ids(1, ids1);
   int cnt = cand_stride_pages;
-  if (cand_pages != nullptr) {
+  if (crow != nullptr) {
     cnt = cand_count ? cand_count[unit] : (n + kPage - 1) / kPage;
     cnt = cnt < cand_stride_pages ? cnt : cand_stride_pages;
   }
+  // validated page ids and their page-table entries
+  auto load_phys = [&](int j, int (&pid)[PB], int (&phys)[PB]) {
 #pragma unroll
-  for (int i = 0; i < kPagesPerWave; ++i) {
-    const bool ok = rank[i] < cnt && pid[i] >= 0 && pid[i] < max_pages && pid[i] * kPage < n;
-    pid[i] = ok ? pid[i] : -1;
-    phys[i] = page_table[static_cast<long>(b) * max_pages + (ok ? pid[i] : 0)];
-  }
-  // codes (one word per group) and {scale, zero} of this lane's token in each page
-  uint32_t cw[kPagesPerWave][NG], mw[kPagesPerWave][NG];
-#pragma unroll
-  for (int i = 0; i < kPagesPerWave; ++i) {
-    const bool ok = pid[i] >= 0 && phys_ok(phys[i], num_phys);
-    const long row = ok ? (static_cast<long>(phys[i]) * Hkv + g) * kPage + tok_in_page : 0;
-    const uint32_t* crow = reinterpret_cast<const uint32_t*>(codes + row * (D / 2));
-#pragma unroll
-    for (int grp = 0; grp < NG; ++grp) {
-      cw[i][grp] = crow[grp * 4 + c4];
-      mw[i][grp] = meta[row * NG + grp];
+    for (int i = 0; i < PB; ++i) {
+      const int r = rank_of(j, i);
+      const bool ok = r < page_end && r < cnt && pid[i] >= 0 && pid[i] < max_pages &&
+                      pid[i] * kPage < n;
+      pid[i] = ok ? pid[i] : -1;
+      phys[i] = page_table[static_cast<long>(b) * max_pages + (ok ? pid[i] : 0)];
     }
-    if (!ok) pid[i] = -1;
-  }
+  };
+  // this lane's codes (virtual group c4 of its token's row) and its group's {scale, zero}
+  auto load_codes = [&](int (&pid)[PB], const int (&phys)[PB], CodeWords<VG / 8> (&cw)[PB],
+                        uint32_t (&mw)[PB]) {
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const bool ok = pid[i] >= 0 && phys_ok(phys[i], num_phys);
+      pid[i] = ok ? pid[i] : -1;
+      const long row = ok ? (static_cast<long>(phys[i]) * Hkv + g) * kPage + tok_in_page : 0;
+      cw[i] = load_words<VG / 8>(reinterpret_cast<const uint32_t*>(codes + row * (D / 2)) +
+                                 c4 * (VG / 8));
+      mw[i] = meta[row * NG + c4 * VG / 32];
+    }
+  };
+  int phys0[PB], phys1[PB];
+  CodeWords<VG / 8> cw0[PB];
+  uint32_t mw0[PB];
+  load_phys(0, ids0, phys0);
+  load_codes(ids0, phys0, cw0, mw0);
+  if (n_batches > 1) load_phys(1, ids1, phys1);
 
   // the group's queries and their per-group sums
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
@@ -125,173 +179,245 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     qsum[h][grp] = acc;
   }
   __syncthreads();
-  // A operands: row = head lane%16 (zero past G), channel slots as in mfma_channel
-  f16x4 qa[NG][2];
-  const int qh = lane % 16;
+  // A operands: row (vg, h) = (lane%16 / 4, lane%16 % 4 + 4 hb), nonzero only on the
+  // channels of virtual group vg and for h < G
+  f16x4 qa[NHB][MPT];
+  {
+    const int vg = (lane % 16) / 4;
 #pragma unroll
-  for (int grp = 0; grp < NG; ++grp)
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int h = (lane % 16) % 4 + 4 * hb;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < MPT; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qa[grp][m][e] = qh < G ? qs[qh < G ? qh : 0][grp * 32 + mfma_channel(c4, m, e)]
-                               : static_cast<f16>(0.f);
-  float qg[NG][HR];  // Q_grp of this lane's output heads 4 c4 + r
+        for (int e = 0; e < 4; ++e)
+          qa[hb][m][e] = (vg == c4 && h < G) ? qs[h < G ? h : 0][mfma_channel(c4, VG, m, e)]
+                                             : static_cast<f16>(0.f);
+    }
+  }
+  // Q_grp * zero enters once per real group: by the lane group holding its first channels
+  const bool adds_zero = (c4 * VG) % 32 == 0;
+  float qg[NHB][4];  // Q of this lane's group for heads r + 4 hb
 #pragma unroll
-  for (int grp = 0; grp < NG; ++grp)
+  for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int r = 0; r < HR; ++r) {
-      const int h = 4 * c4 + r;
-      qg[grp][r] = h < G ? qsum[h < G ? h : 0][grp] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int h = r + 4 * hb;
+      qg[hb][r] = (h < G && adds_zero) ? qsum[h < G ? h : 0][c4 * VG / 32] : 0.f;
     }
   TWL_PHASE(1);
 
-  const int wave_slot0 = (chunk * kEstWaves + wave) * kPagesPerWave * kPage;
-  float s[kPagesPerWave][HR];
+  float run_m[NHB], run_l[NHB];  // online max and sum of exp of this lane's head(s)
 #pragma unroll
-  for (int i = 0; i < kPagesPerWave; ++i) {
-    float acc[HR];
-#pragma unroll
-    for (int r = 0; r < HR; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int grp = 0; grp < NG; ++grp) {
-      const uint32_t w = cw[i][grp];
-      uint32_t bw[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) bw[k] = codes_to_f16x2((w >> (4 * k)) & 0x000f000fu);
-      const f16x4 b0 = __builtin_bit_cast(f16x4, u32x2{bw[0], bw[1]});
-      const f16x4 b1 = __builtin_bit_cast(f16x4, u32x2{bw[2], bw[3]});
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-      d = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[grp][0], b0, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[grp][1], b1, d, 0, 0, 0);
-      const float scale = h2f(static_cast<uint16_t>(mw[i][grp] & 0xffffu));
-      const float zero = h2f(static_cast<uint16_t>(mw[i][grp] >> 16));
-#pragma unroll
-      for (int r = 0; r < HR; ++r) acc[r] = fmaf(scale, d[r], fmaf(zero, qg[grp][r], acc[r]));
-    }
-    const int t = pid[i] * kPage + tok_in_page;
-    const bool valid = pid[i] >= 0 && t < n;
-#pragma unroll
-    for (int r = 0; r < HR; ++r) s[i][r] = valid ? sm_scale * acc[r] : -INFINITY;
+  for (int hb = 0; hb < NHB; ++hb) {
+    run_m[hb] = -INFINITY;
+    run_l[hb] = 0.f;
   }
-  TWL_PHASE(2);
-  // logits rows, then (max, sum exp) of this chunk per head
-  const bool head_lane = 4 * c4 < G;
+  for (int j = 0; j < n_batches; ++j) {
+    int ids2[PB];
+    if (j + 2 < n_batches) load_ids(j + 2, ids2);
+    CodeWords<VG / 8> cw1[PB];
+    uint32_t mw1[PB];
+    if (j + 1 < n_batches) load_codes(ids1, phys1, cw1, mw1);
+
+    float s[PB][NHB];
 #pragma unroll
-  for (int i = 0; i < kPagesPerWave; ++i) {
-    const int slot = wave_slot0 + i * kPage + tok_in_page;
-    if (head_lane && slot < n_slots) {
+    for (int i = 0; i < PB; ++i) {
+      // B operands of the tile: two instructions per 32-bit word of codes
+      f16x4 bq[MPT];
 #pragma unroll
-      for (int r = 0; r < HR; ++r) {
-        const int h = 4 * c4 + r;
-        if (h < G) logits[(static_cast<long>(b) * Hq + g * G + h) * n_slots + slot] = s[i][r];
+      for (int wi = 0; wi < VG / 8; ++wi) {
+        const uint32_t w = cw0[i].w[wi];
+        uint32_t bw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bw[k] = codes_to_f16x2((w >> (4 * k)) & 0x000f000fu);
+        bq[2 * wi] = __builtin_bit_cast(f16x4, u32x2{bw[0], bw[1]});
+        bq[2 * wi + 1] = __builtin_bit_cast(f16x4, u32x2{bw[2], bw[3]});
+      }
+      const float scale = h2f(static_cast<uint16_t>(mw0[i] & 0xffffu));
+      const float zero = h2f(static_cast<uint16_t>(mw0[i] >> 16));
+      const int t = ids0[i] * kPage + tok_in_page;
+      const bool valid = ids0[i] >= 0 && t < n;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < MPT; ++m)
+          d = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[hb][m], bq[m], d, 0, 0, 0);
+        // this lane group's term for heads r + 4 hb, summed over the four lane groups
+        float tot[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = fmaf(scale, d[r], zero * qg[hb][r]);
+          {
+            const auto x = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v),
+                                                            __builtin_bit_cast(int, v), false, false);
+            v = __builtin_bit_cast(float, static_cast<int>(x[0])) +
+                __builtin_bit_cast(float, static_cast<int>(x[1]));
+          }
+          {
+            const auto x = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v),
+                                                            __builtin_bit_cast(int, v), false, false);
+            v = __builtin_bit_cast(float, static_cast<int>(x[0])) +
+                __builtin_bit_cast(float, static_cast<int>(x[1]));
+          }
+          tot[r] = v;
+        }
+        // lane group c4 keeps head c4 + 4 hb
+        const float mine = c4 == 0 ? tot[0] : c4 == 1 ? tot[1] : c4 == 2 ? tot[2] : tot[3];
+        s[i][hb] = (valid && c4 + 4 * hb < G) ? sm_scale * mine : -INFINITY;
+      }
+      // logits row entries (every slot of the chunk is written, -inf when not a candidate)
+      const int slot = rank_of(j, i) * kPage + tok_in_page;
+      if (rank_of(j, i) < page_end) {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          const int h = c4 + 4 * hb;
+          if (h < G) logits[(static_cast<long>(b) * Hq + g * G + h) * n_slots + slot] = s[i][hb];
+        }
       }
     }
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      float bm = s[0][hb];
+#pragma unroll
+      for (int i = 1; i < PB; ++i) bm = fmaxf(bm, s[i][hb]);
+      const float mn = fmaxf(run_m[hb], bm);
+      if (mn > -INFINITY) {
+        float l = run_m[hb] > -INFINITY ? run_l[hb] * expf(run_m[hb] - mn) : 0.f;
+#pragma unroll
+        for (int i = 0; i < PB; ++i) l += s[i][hb] > -INFINITY ? expf(s[i][hb] - mn) : 0.f;
+        run_l[hb] = l;
+        run_m[hb] = mn;
+      }
+    }
+    // rotate the pipeline: batch j + 1 (codes in flight) becomes current, then batch j + 2
+    // (page ids in hand) gets its page-table entries
+    if (j + 1 < n_batches) {
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        ids0[i] = ids1[i];
+        cw0[i] = cw1[i];
+        mw0[i] = mw1[i];
+      }
+    }
+    if (j + 2 < n_batches) {
+      load_phys(j + 2, ids2, phys1);
+#pragma unroll
+      for (int i = 0; i < PB; ++i) ids1[i] = ids2[i];
+    }
   }
-  // per head: max over this wave's 64 slots (4 pages in registers, 16 tokens across the row)
-  float wm[HR];
+  TWL_PHASE(2);
+  // (max, sum exp) per head: over the row's 16 tokens, then over the waves
 #pragma unroll
-  for (int r = 0; r < HR; ++r) {
-    float v = s[0][r];
-#pragma unroll
-    for (int i = 1; i < kPagesPerWave; ++i) v = fmaxf(v, s[i][r]);
-    wm[r] = group_reduce<16>(v, OpMax());
-  }
-  if (head_lane && tok_in_page == 0) {
-#pragma unroll
-    for (int r = 0; r < HR; ++r)
-      if (4 * c4 + r < G) red_m[wave][4 * c4 + r] = wm[r];
-  }
-  __syncthreads();
-  float e_sum[HR];
-  float M[HR];
-#pragma unroll
-  for (int r = 0; r < HR; ++r) {
-    const int h = 4 * c4 + r < G ? 4 * c4 + r : 0;
-    float m = red_m[0][h];
-#pragma unroll
-    for (int w2 = 1; w2 < kEstWaves; ++w2) m = fmaxf(m, red_m[w2][h]);
-    M[r] = m;
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < kPagesPerWave; ++i)
-      acc += (s[i][r] > -INFINITY && m > -INFINITY) ? expf(s[i][r] - m) : 0.f;
-    e_sum[r] = group_reduce<16>(acc, OpSum());
-  }
-  if (head_lane && tok_in_page == 0) {
-#pragma unroll
-    for (int r = 0; r < HR; ++r)
-      if (4 * c4 + r < G) red_l[wave][4 * c4 + r] = e_sum[r];
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float M = group_reduce<16>(run_m[hb], OpMax());
+    const float l = run_m[hb] > -INFINITY ? run_l[hb] * expf(run_m[hb] - M) : 0.f;
+    const float L = group_reduce<16>(l, OpSum());
+    const int h = c4 + 4 * hb;
+    if (h < G && tok_in_page == 0) {
+      red_m[wave][h] = M;
+      red_l[wave][h] = L;
+    }
   }
   __syncthreads();
   if (threadIdx.x < G) {
     const int h = threadIdx.x;
-    float m = red_m[0][h], l = 0.f;
+    float M = red_m[0][h];
 #pragma unroll
-    for (int w2 = 1; w2 < kEstWaves; ++w2) m = fmaxf(m, red_m[w2][h]);
+    for (int w2 = 1; w2 < kEstWaves; ++w2) M = fmaxf(M, red_m[w2][h]);
+    float L = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kEstWaves; ++w2) l += red_l[w2][h];
-    partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(m, l);
+    for (int w2 = 0; w2 < kEstWaves; ++w2) L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * expf(red_m[w2][h] - M) : 0.f;
+    partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(M, L);
   }
-  (void)M;
   TWL_PHASE(3);
 }
 
 // w = exp(s - M) / L with (M, L) merged from the row's chunk partials; invalid slots hold
-// s = -inf and come out as exactly 0.
-__global__ __launch_bounds__(kEstChunk) void estimate_normalize_kernel(
+// s = -inf and come out as exactly 0. Each thread takes 16 consecutive weights; wave 0
+// merges the partials while every thread's loads are in flight.
+__global__ __launch_bounds__(kNormThreads) void estimate_normalize_kernel(
     float* __restrict__ weights, const float2* __restrict__ partials, int n_chunks, int n_slots) {
-  __shared__ float red[kEstChunk / kWave];
-  const long hrow = static_cast<long>(blockIdx.y) * gridDim.z + blockIdx.z;
-  const int slot = blockIdx.x * kEstChunk + threadIdx.x;
-  float* w = weights + hrow * n_slots + slot;
-  const float s = slot < n_slots ? *w : -INFINITY;  // issued before the partials
-  const float2* pr = partials + hrow * n_chunks;
-  float m = -INFINITY, l = 0.f;
-  // this thread's share of the chunk partials, merged on the fly
-  for (int i = threadIdx.x; i < n_chunks; i += blockDim.x) {
-    const float2 v = pr[i];
-    if (v.x > -INFINITY) {
-      const float mn = fmaxf(m, v.x);
-      l = (m > -INFINITY ? l * expf(m - mn) : 0.f) + v.y * expf(v.x - mn);
-      m = mn;
+  __shared__ float s_ml[2];
+  const long hrow = blockIdx.y;
+  const int first = blockIdx.x * kNormSlots + threadIdx.x * 16;
+  float* w = weights + hrow * n_slots;
+  f32x4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int sl = first + 4 * k;  // n_slots is a multiple of 16
+    v[k] = *reinterpret_cast<const f32x4*>(w + (sl < n_slots ? sl : 0));
+  }
+  if (threadIdx.x < kWave) {
+    const float2* pr = partials + hrow * n_chunks;
+    float m = -INFINITY, l = 0.f;
+    for (int i = threadIdx.x; i < n_chunks; i += kWave) {
+      const float2 p = pr[i];
+      if (p.x > -INFINITY) {
+        const float mn = fmaxf(m, p.x);
+        l = (m > -INFINITY ? l * expf(m - mn) : 0.f) + p.y * expf(p.x - mn);
+        m = mn;
+      }
+    }
+    const float M = wave_max(m);
+    const float L = wave_sum(m > -INFINITY ? l * expf(m - M) : 0.f);
+    if (threadIdx.x == 0) {
+      s_ml[0] = M;
+      s_ml[1] = L;
     }
   }
-  const float M = block_max<kEstChunk>(m, red);
-  const float L = block_sum<kEstChunk>(m > -INFINITY ? l * expf(m - M) : 0.f, red);
-  if (slot >= n_slots) return;
-  *w = (L > 0.f && s > -INFINITY) ? expf(s - M) / L : 0.f;
+  __syncthreads();
+  const float M = s_ml[0], L = s_ml[1];
+  if (first >= n_slots) return;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (L > 0.f && v[k][e] > -INFINITY) ? expf(v[k][e] - M) / L : 0.f;
+    *reinterpret_cast<f32x4*>(w + first + 4 * k) = o;
+  }
 }
 
 template <int D, int G>
 void logits_launch(const Layout& L, const void* q, const uint8_t* codes, const void* meta,
                    const int32_t* cand_pages, const int32_t* cand_count, int stride,
-                   float sm_scale, float* weights, float2* partials, int n_chunks,
-                   hipStream_t s) {
+                   float sm_scale, float* weights, float2* partials, int chunk_pages,
+                   int n_chunks, hipStream_t s) {
   estimate_logits_kernel<D, G><<<dim3(n_chunks, L.Hkv, L.B), kEstChunk, 0, s>>>(
       static_cast<const uint16_t*>(q), codes, static_cast<const uint32_t*>(meta), L.page_table,
       L.seq_lens, cand_pages, cand_count, stride, L.Hkv, L.max_pages, L.num_phys, sm_scale,
-      weights, partials, n_chunks);
+      weights, partials, chunk_pages, n_chunks);
 }
 
 template <int D>
 void logits_dispatch_g(const Layout& L, const void* q, const uint8_t* codes, const void* meta,
                        const int32_t* cand_pages, const int32_t* cand_count, int stride,
-                       float sm_scale, float* weights, float2* partials, int n_chunks,
-                       hipStream_t s) {
+                       float sm_scale, float* weights, float2* partials, int chunk_pages,
+                       int n_chunks, hipStream_t s) {
   switch (L.G()) {
-    case 1: logits_launch<D, 1>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, n_chunks, s); break;
-    case 2: logits_launch<D, 2>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, n_chunks, s); break;
-    case 4: logits_launch<D, 4>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, n_chunks, s); break;
-    default: logits_launch<D, 8>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, n_chunks, s); break;
+    case 1: logits_launch<D, 1>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+    case 2: logits_launch<D, 2>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+    case 4: logits_launch<D, 4>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+    default: logits_launch<D, 8>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
   }
+}
+
+// Candidate pages per logits work-group: about TWL_EST_TARGET_BLOCKS work-groups over all
+// candidate pages, at least one batch per wave and at most TWL_EST_MAX_CHUNK_PAGES.
+int estimate_chunk_pages(const Layout& L, int cand_stride_pages) {
+  const long total = static_cast<long>(L.B) * L.Hkv * cand_stride_pages;
+  const long want = (total + TWL_EST_TARGET_BLOCKS - 1) / TWL_EST_TARGET_BLOCKS;
+  long c = kEstWaves * kEstBatch;
+  while (c < want && c < TWL_EST_MAX_CHUNK_PAGES) c <<= 1;
+  return static_cast<int>(c);
 }
 
 }  // namespace
 
 size_t estimate_workspace_bytes(const Layout& L, int cand_stride_pages) {
-  const long n_slots = static_cast<long>(cand_stride_pages) * kPage;
-  const long n_chunks = (n_slots + kEstChunk - 1) / kEstChunk;
+  const int cp = estimate_chunk_pages(L, cand_stride_pages);
+  const long n_chunks = (static_cast<long>(cand_stride_pages) + cp - 1) / cp;
   return align_up(static_cast<size_t>(L.B) * L.Hq * n_chunks * sizeof(float2), 256);
 }
 
@@ -300,19 +426,20 @@ hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes,
                            int cand_stride_pages, float sm_scale, float* weights, void* ws,
                            hipStream_t s) {
   const int n_slots = cand_stride_pages * kPage;
-  const int n_chunks = (n_slots + kEstChunk - 1) / kEstChunk;
+  const int cp = estimate_chunk_pages(L, cand_stride_pages);
+  const int n_chunks = (cand_stride_pages + cp - 1) / cp;
   float2* partials = static_cast<float2*>(stage_scratch(ws, L));
   if (L.d == 128) {
     logits_dispatch_g<128>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
-                           sm_scale, weights, partials, n_chunks, s);
+                           sm_scale, weights, partials, cp, n_chunks, s);
   } else {
     logits_dispatch_g<64>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
-                          sm_scale, weights, partials, n_chunks, s);
+                          sm_scale, weights, partials, cp, n_chunks, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  estimate_normalize_kernel<<<dim3(n_chunks, L.B, L.Hq), kEstChunk, 0, s>>>(weights, partials,
-                                                                          n_chunks, n_slots);
+  const dim3 grid((n_slots + kNormSlots - 1) / kNormSlots, L.B * L.Hq);
+  estimate_normalize_kernel<<<grid, kNormThreads, 0, s>>>(weights, partials, n_chunks, n_slots);
   return hipGetLastError();
 }
 
