@@ -70,22 +70,24 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ kept_count, int kept_stride, int Hkv, int max_pages,
-    int num_phys, float scale_log2, float* __restrict__ partials,
+    int num_phys, float scale_log2, float* __restrict__ part_o, float2* __restrict__ part_ml,
     int n_chunks, int chunk_tokens, uint16_t* __restrict__ out) {
   constexpr int LPT = D / 8;        // lanes per token row
   constexpr int TPW = kWave / LPT;  // token rows per wave per load
   constexpr int U = kDecUnroll;
   constexpr int STEP = TPW * U;     // tokens per wave per batch
   constexpr int BSTEP = decode_batch_tokens(D);
-  constexpr int PSTRIDE = D + 4;    // floats per (chunk, head) partial: m, l, 2 pad, o[D]
   __shared__ float s_m[kDecWaves][G], s_l[kDecWaves][G];
   __shared__ float s_acc[kDecWaves][G][D];
   TWL_PHASE(0);
   TWL_SPAN_BEGIN();
 
-  const int b = blockIdx.z;
-  const int g = blockIdx.y;
-  const int chunk = blockIdx.x;
+  // work-groups are numbered chunk-major (every KV head's first chunk, then every second
+  // chunk, ...), so that chunks past a short kept list, which exit at once, are dispatched
+  // last instead of holding slots ahead of useful work
+  const int b = blockIdx.y;
+  const int g = blockIdx.x % Hkv;
+  const int chunk = blockIdx.x / Hkv;
   const long unit = static_cast<long>(b) * Hkv + g;
   const int Hq = Hkv * G;
   const long head0 = static_cast<long>(b) * Hq + g * G;
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     return;
   }
   if (t0 >= K) return;
+  TWL_PHASE(4);
   const int t1 = min(K, t0 + chunk_tokens);
   const int nc = (K + chunk_tokens - 1) / chunk_tokens;
   const int n_batches = (t1 - t0 + BSTEP - 1) / BSTEP;
@@ -174,6 +177,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   bool live0[U];
   u32x4 kv0[U], vv0[U];
   load_kv(phys0, tok0, live0, kv0, vv0);
+  TWL_PHASE(5);
   if (n_batches > 1) load_rows(1, ids1, phys1, tok1);
 
   for (int j = 0; j < n_batches; ++j) {
@@ -197,6 +201,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
         s[u][h] = live0[u] ? d * scale_log2 : -INFINITY;
       }
     }
+    if (j == 0) TWL_PHASE(6);
     // one running max per head for the whole wave: the token groups' batch maxima are
     // combined across groups, so every group's (l, acc) stays on the same scale
     float pr[U][G];
@@ -275,14 +280,11 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
           }
           *reinterpret_cast<u32x4*>(out + (head0 + h) * D + c0) = o;
         } else {
-          float* dst = partials + ((head0 + h) * n_chunks + chunk) * PSTRIDE;
-          if (sub == 0) {
-            dst[0] = m[h];
-            dst[1] = l[h];
-          }
+          const long pidx = (head0 + h) * n_chunks + chunk;
+          if (sub == 0) part_ml[pidx] = make_float2(m[h], l[h]);
+          float* dst = part_o + pidx * D;
+          *reinterpret_cast<f32x4*>(dst + c0) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
           *reinterpret_cast<f32x4*>(dst + 4 + c0) =
-              f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-          *reinterpret_cast<f32x4*>(dst + 8 + c0) =
               f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
         }
       }
@@ -318,12 +320,9 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
         const float o = L > 0.f ? A / L : 0.f;
         out[(head0 + h) * D + c] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
       } else {
-        float* dst = partials + ((head0 + h) * n_chunks + chunk) * PSTRIDE;
-        if (c == 0) {
-          dst[0] = M;
-          dst[1] = L;
-        }
-        dst[4 + c] = A;
+        const long pidx = (head0 + h) * n_chunks + chunk;
+        if (c == 0) part_ml[pidx] = make_float2(M, L);
+        part_o[pidx * D + c] = A;
       }
     }
   }
@@ -333,12 +332,14 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 
 // Merge of the chunk partials when they are more than one: one wave per (sequence, query
 // head, 16-channel slice). Lane i takes chunks i, i + 64, ... with a running (max, sum, o)
-// of its own; the lanes are then combined on the common maximum.
+// of its own; the lanes are then combined on the common maximum. The (max, sum) pairs sit
+// in their own compact array and each chunk's o in a 512-byte record, so every byte of the
+// partials is fetched once.
 template <int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
-    const float* __restrict__ partials, const int32_t* __restrict__ kept_count, int kept_stride,
-    int Hkv, int G, int n_chunks, int chunk_tokens, uint16_t* __restrict__ out) {
-  constexpr int PSTRIDE = D + 4;
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml,
+    const int32_t* __restrict__ kept_count, int kept_stride, int Hkv, int G, int n_chunks,
+    int chunk_tokens, uint16_t* __restrict__ out) {
   __shared__ float s_acc[kWave][kMergeSlice + 1];
   const int slice = blockIdx.x;
   const int h = blockIdx.y;
@@ -350,21 +351,22 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
   const int nc = (K + chunk_tokens - 1) / chunk_tokens;
   if (nc <= 1) return;  // finished by the partial kernel
   const int lane = lane_id();
-  const float* ph = partials + (static_cast<long>(b) * Hq + h) * n_chunks * PSTRIDE;
+  const long hrow = static_cast<long>(b) * Hq + h;
+  const float2* ml = part_ml + hrow * n_chunks;
+  const float* po = part_o + hrow * n_chunks * D + slice * kMergeSlice;
   float M = -INFINITY, L = 0.f;
   float acc[kMergeSlice];
 #pragma unroll
   for (int c = 0; c < kMergeSlice; ++c) acc[c] = 0.f;
   for (int i = lane; i < nc; i += kWave) {
-    const float* pi = ph + static_cast<long>(i) * PSTRIDE;
-    const float mi = pi[0], li = pi[1];
+    const float2 mi = ml[i];
     f32x4 a[kMergeSlice / 4];
 #pragma unroll
     for (int v = 0; v < kMergeSlice / 4; ++v)
-      a[v] = *reinterpret_cast<const f32x4*>(pi + 4 + slice * kMergeSlice + 4 * v);
-    const float Mn = fmaxf(M, mi);
-    const float fo = rescale(M, Mn), fi = rescale(mi, Mn);
-    L = L * fo + li * fi;
+      a[v] = *reinterpret_cast<const f32x4*>(po + static_cast<long>(i) * D + 4 * v);
+    const float Mn = fmaxf(M, mi.x);
+    const float fo = rescale(M, Mn), fi = rescale(mi.x, Mn);
+    L = L * fo + mi.y * fi;
 #pragma unroll
     for (int v = 0; v < kMergeSlice / 4; ++v) {
 #pragma unroll
@@ -382,33 +384,32 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     float t = 0.f;
     for (int r = 0; r < kWave; ++r) t += s_acc[r][lane];
     const float o = L > 0.f ? t / L : 0.f;
-    out[(static_cast<long>(b) * Hq + h) * D + slice * kMergeSlice + lane] =
-        __builtin_bit_cast(uint16_t, static_cast<f16>(o));
+    out[hrow * D + slice * kMergeSlice + lane] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
   }
 }
 
 template <int D, int G>
 void decode_launch(const Layout& L, const void* q, const void* k, const void* v,
                    const int32_t* kept, const int32_t* kept_count, int kept_stride,
-                   float scale_log2, float* partials, int n_chunks, int ch, void* out,
-                   hipStream_t s) {
-  sparse_decode_kernel<D, G><<<dim3(n_chunks, L.Hkv, L.B), kDecThreads, 0, s>>>(
+                   float scale_log2, float* part_o, float2* part_ml, int n_chunks, int ch,
+                   void* out, hipStream_t s) {
+  sparse_decode_kernel<D, G><<<dim3(n_chunks * L.Hkv, L.B), kDecThreads, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), L.page_table, L.seq_lens, kept, kept_count, kept_stride,
-      L.Hkv, L.max_pages, L.num_phys, scale_log2, partials, n_chunks, ch,
+      L.Hkv, L.max_pages, L.num_phys, scale_log2, part_o, part_ml, n_chunks, ch,
       static_cast<uint16_t*>(out));
 }
 
 template <int D>
 void decode_dispatch_g(const Layout& L, const void* q, const void* k, const void* v,
                        const int32_t* kept, const int32_t* kept_count, int kept_stride,
-                       float scale_log2, float* partials, int n_chunks, int ch, void* out,
-                       hipStream_t s) {
+                       float scale_log2, float* part_o, float2* part_ml, int n_chunks, int ch,
+                       void* out, hipStream_t s) {
   switch (L.G()) {
-    case 1: decode_launch<D, 1>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
-    case 2: decode_launch<D, 2>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
-    case 4: decode_launch<D, 4>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
-    default: decode_launch<D, 8>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, partials, n_chunks, ch, out, s); break;
+    case 1: decode_launch<D, 1>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, part_o, part_ml, n_chunks, ch, out, s); break;
+    case 2: decode_launch<D, 2>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, part_o, part_ml, n_chunks, ch, out, s); break;
+    case 4: decode_launch<D, 4>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, part_o, part_ml, n_chunks, ch, out, s); break;
+    default: decode_launch<D, 8>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, part_o, part_ml, n_chunks, ch, out, s); break;
   }
 }
 
@@ -429,7 +430,8 @@ int decode_chunk_tokens(const Layout& L, int kept_stride) {
 size_t decode_workspace_bytes(const Layout& L, int kept_stride) {
   const int ch = decode_chunk_tokens(L, kept_stride);
   const long n_chunks = (static_cast<long>(kept_stride) + ch - 1) / ch;
-  return align_up(static_cast<size_t>(L.B) * L.Hq * n_chunks * (L.d + 4) * sizeof(float), 256);
+  // o records [B * Hq, n_chunks, d], then (max, sum) pairs [B * Hq, n_chunks]
+  return align_up(static_cast<size_t>(L.B) * L.Hq * n_chunks * (L.d + 2) * sizeof(float), 256);
 }
 
 hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_cache,
@@ -438,24 +440,25 @@ hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_ca
                                 void* out, void* ws, hipStream_t s) {
   const int ch = decode_chunk_tokens(L, kept_stride);
   const int n_chunks = (kept_stride + ch - 1) / ch;
-  auto* partials = static_cast<float*>(stage_scratch(ws, L));
+  auto* part_o = static_cast<float*>(stage_scratch(ws, L));
+  auto* part_ml = reinterpret_cast<float2*>(part_o + static_cast<long>(L.B) * L.Hq * n_chunks * L.d);
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (L.d == 128) {
     decode_dispatch_g<128>(L, q, k_cache, v_cache, kept, kept_count, kept_stride, scale_log2,
-                           partials, n_chunks, ch, out, s);
+                           part_o, part_ml, n_chunks, ch, out, s);
   } else {
     decode_dispatch_g<64>(L, q, k_cache, v_cache, kept, kept_count, kept_stride, scale_log2,
-                          partials, n_chunks, ch, out, s);
+                          part_o, part_ml, n_chunks, ch, out, s);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto* o = static_cast<uint16_t*>(out);
   const dim3 grid(L.d / kMergeSlice, L.Hq, L.B);
   if (L.d == 128) {
-    decode_merge_kernel<128><<<grid, kWave, 0, s>>>(partials, kept_count, kept_stride, L.Hkv,
+    decode_merge_kernel<128><<<grid, kWave, 0, s>>>(part_o, part_ml, kept_count, kept_stride, L.Hkv,
                                                     L.G(), n_chunks, ch, o);
   } else {
-    decode_merge_kernel<64><<<grid, kWave, 0, s>>>(partials, kept_count, kept_stride, L.Hkv,
+    decode_merge_kernel<64><<<grid, kWave, 0, s>>>(part_o, part_ml, kept_count, kept_stride, L.Hkv,
                                                    L.G(), n_chunks, ch, o);
   }
   return hipGetLastError();
