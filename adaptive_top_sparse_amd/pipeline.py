@@ -149,3 +149,26 @@ def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[floa
         twilight_sparse_decode(lay, c.q, c.k_cache, c.v_cache, buf.kept, buf.kept_count,
                                stride * PAGE_SIZE, sm_scale, buf.out, buf.workspace,
                                stream=stream)
+
+
+def baseline_kept(c: DeviceCache, buf: StepBuffers, mode: str):
+    """Kept-token lists for the comparison steps that run on the same decode kernel:
+    "dense" keeps every token of each sequence, "quest" every token of the pages the Quest
+    selector chose in `buf` (a step must have run). Returns (kept [B, Hkv, stride] int32,
+    kept_count [B, Hkv] int32, stride); tokens at or past a sequence's end are skipped by the
+    decode itself."""
+    dev = c.q.device
+    if mode == "dense":
+        stride = c.max_pages * PAGE_SIZE
+        kept = torch.arange(stride, dtype=torch.int32, device=dev).expand(c.B, c.Hkv, stride)
+        count = c.seq_lens.clamp(min=0).to(torch.int32)[:, None].expand(c.B, c.Hkv)
+    elif mode == "quest":
+        if c.budget is None:
+            raise ValueError("the Quest-only list needs a Quest budget")
+        stride = c.budget * PAGE_SIZE
+        offs = torch.arange(PAGE_SIZE, dtype=torch.int32, device=dev)
+        kept = (buf.sel_pages[..., None] * PAGE_SIZE + offs).reshape(c.B, c.Hkv, stride)
+        count = buf.sel_count * PAGE_SIZE
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    return kept.contiguous(), count.contiguous(), stride

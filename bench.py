@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the dense and Quest-only comparison steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling HBM "
                          "traffic counters) and exit")
@@ -117,6 +119,59 @@ def stage_bytes(c, buf, d):
     out["twilight_topp_select"] = int(cand.sum() * G * 4 + kept.sum() * 4)
     out["twilight_sparse_decode"] = int(kept.sum() * (2 * d * 2 + 4) + 2 * qo)
     return out, int(cand.sum()), int(kept.sum())
+
+
+def time_baselines(reps, bufs, stream, steps, warmup, twilight_us):
+    """Dense and Quest-only decode steps on the same kernels, hipGraph replays in rotation
+    over the same layer replicas: dense = twilight_sparse_decode over every token; Quest-only
+    = quest_select_pages + twilight_sparse_decode over every token of the selected pages."""
+    import torch
+    import adaptive_top_sparse_amd as twl
+    from adaptive_top_sparse_amd import pipeline
+    out = {"twilight_us": twilight_us}
+    modes = ["dense"] + (["quest"] if reps[0].budget is not None else [])
+    for mode in modes:
+        graphs, keep = [], []
+        for c, buf in zip(reps, bufs):
+            kept, count, stride = pipeline.baseline_kept(c, buf, mode)
+            lay = c.layout()
+            ws = torch.zeros(twl.twilight_workspace_size(lay, stride // twl.PAGE_SIZE),
+                             dtype=torch.uint8, device=c.q.device)
+            o = torch.empty_like(buf.out)
+            keep.append((kept, count, ws, o))
+
+            def run(c=c, buf=buf, kept=kept, count=count, ws=ws, o=o, stride=stride, lay=lay):
+                if mode == "quest":
+                    twl.quest_select_pages(lay, c.q, c.page_minmax, c.budget, buf.sel_pages,
+                                           buf.sel_count, ws, stream=stream)
+                twl.twilight_sparse_decode(lay, c.q, c.k_cache, c.v_cache, kept, count, stride,
+                                           pipeline.default_sm_scale(c.d), o, ws, stream=stream)
+            with torch.cuda.stream(stream):
+                run()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                run()
+            graphs.append(g)
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(steps):
+                graphs[i % len(graphs)].replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        name = "dense_us" if mode == "dense" else "quest_only_us"
+        out[name] = us
+        out["speedup_vs_" + ("dense" if mode == "dense" else "quest")] = us / twilight_us
+        del graphs, keep
+    out["note"] = ("same decode kernel; Quest-only token lists expanded once outside the "
+                   "timed region (fixed q)")
+    return out
 
 
 def cpu_baseline(w, p, seconds):
@@ -292,8 +347,13 @@ def main():
         "stage_bytes": per_stage_bytes,
         "cache_build_ms": build_ms,
         "roofline": roofline,
+        "baselines": None,
         "cpu_baseline": None,
     }
+    if not args.no_baselines:
+        print("[bench] timing the dense and Quest-only steps", file=sys.stderr, flush=True)
+        res["baselines"] = time_baselines(reps, bufs, stream, args.steps, args.warmup,
+                                          graph_ms * 1e3)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, p, args.cpu_seconds)
