@@ -26,7 +26,7 @@ TWL_ERR_LAUNCH = -4
 
 EXPORTED = ("twilight_quantize_keys", "quest_page_bounds", "quest_select_pages",
             "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode",
-            "twilight_workspace_size", "twilight_status_string")
+            "twilight_append_keys", "twilight_workspace_size", "twilight_status_string")
 
 
 class TwilightError(RuntimeError):
@@ -63,7 +63,8 @@ def lib():
         L.twilight_estimate_weights.argtypes = [LP, P, P, P, P, P, I32, F, P, P, SZ, P]
         L.twilight_topp_select.argtypes = [LP, P, P, P, I32, F, P, P, P, P, SZ, P]
         L.twilight_sparse_decode.argtypes = [LP, P, P, P, P, P, I32, F, P, P, SZ, P]
-        for name in EXPORTED[:6]:
+        L.twilight_append_keys.argtypes = [LP, P, P, P, P, P, P]
+        for name in EXPORTED[:7]:
             getattr(L, name).restype = ctypes.c_int
         L.twilight_workspace_size.argtypes = [LP, I32]
         L.twilight_workspace_size.restype = ctypes.c_size_t
@@ -146,6 +147,17 @@ def quest_page_bounds(layout: Layout, k_cache, page_minmax, token_begin=None,
         _ptr(token_begin, torch.int32, "token_begin"),
         _ptr(page_minmax, torch.float16, "page_minmax"), _stream(stream))
     _check("quest_page_bounds", st)
+
+
+def twilight_append_keys(layout: Layout, k_cache, token_begin, k_codes, k_meta,
+                         page_minmax=None, stream=None) -> None:
+    import torch
+    st = lib().twilight_append_keys(
+        ctypes.byref(layout), _ptr(k_cache, torch.float16, "k_cache"),
+        _ptr(token_begin, torch.int32, "token_begin"), _ptr(k_codes, torch.uint8, "k_codes"),
+        _ptr(k_meta, torch.float16, "k_meta"), _ptr(page_minmax, torch.float16, "page_minmax"),
+        _stream(stream))
+    _check("twilight_append_keys", st)
 
 
 def quest_select_pages(layout: Layout, q, page_minmax, budget_pages: int, sel_pages, sel_count,

@@ -108,6 +108,22 @@ int quest_page_bounds(const twl_layout_t* L, const void* k_cache, const int32_t*
   return launch_status(twl::launch_page_bounds(lay, k_cache, token_begin, page_minmax, stream));
 }
 
+int twilight_append_keys(const twl_layout_t* L, const void* k_cache, const int32_t* token_begin,
+                         uint8_t* k_codes, void* k_meta, void* page_minmax, hipStream_t stream) {
+  Layout lay{};
+  bool empty = false;
+  int st = check_layout(L, &lay, &empty);
+  if (st != TWL_OK) return st;
+  if (k_cache == nullptr || token_begin == nullptr || k_codes == nullptr || k_meta == nullptr)
+    return TWL_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned4(token_begin) || !aligned16(k_codes) || !aligned4(k_meta))
+    return TWL_ERR_INVALID_ARG;
+  if (page_minmax != nullptr && !aligned16(page_minmax)) return TWL_ERR_INVALID_ARG;
+  if (empty) return TWL_OK;
+  return launch_status(
+      twl::launch_append_keys(lay, k_cache, token_begin, k_codes, k_meta, page_minmax, stream));
+}
+
 int quest_select_pages(const twl_layout_t* L, const void* q, const void* page_minmax,
                        int32_t budget_pages, int32_t* sel_pages, int32_t* sel_count,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -35,6 +35,8 @@ hipError_t launch_quantize_keys(const Layout& L, const void* k_cache, const int3
                                 uint8_t* codes, void* meta, hipStream_t s);
 hipError_t launch_page_bounds(const Layout& L, const void* k_cache, const int32_t* token_begin,
                               void* minmax, hipStream_t s);
+hipError_t launch_append_keys(const Layout& L, const void* k_cache, const int32_t* token_begin,
+                              uint8_t* codes, void* meta, void* minmax, hipStream_t s);
 hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
                                int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s);
 hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes, const void* meta,

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import (PAGE_SIZE, make_layout, quest_page_bounds, quest_select_pages,
-               twilight_estimate_weights, twilight_quantize_keys, twilight_sparse_decode,
+               twilight_append_keys, twilight_estimate_weights, twilight_quantize_keys, twilight_sparse_decode,
                twilight_topp_select, twilight_workspace_size)
 
 
@@ -41,6 +41,7 @@ class DeviceCache:
     k_codes: torch.Tensor
     k_meta: torch.Tensor
     page_minmax: Optional[torch.Tensor]
+    last_token: torch.Tensor  # seq_len - 1 (>= 0) per sequence: the newest token
 
     def layout(self):
         return make_layout(self.page_table, self.seq_lens, self.Hq, self.Hkv, self.d,
@@ -53,6 +54,13 @@ class DeviceCache:
     @property
     def cand_stride_pages(self) -> int:
         return self.budget if self.budget is not None else self.max_pages
+
+    def append_last_token(self, stream=None) -> None:
+        """Per-step cache maintenance for the newest token of every sequence (the one at
+        seq_len - 1, whose K/V row the model has written): its int4 codes and its page's
+        bounds."""
+        twilight_append_keys(self.layout(), self.k_cache, self.last_token, self.k_codes,
+                             self.k_meta, self.page_minmax, stream=stream)
 
     def build_caches(self, stream=None) -> None:
         """Quantize every key and compute every page's bounds (prefill-time maintenance)."""
@@ -90,7 +98,8 @@ def upload(w, device="cuda", with_bounds: Optional[bool] = None) -> DeviceCache:
         k_codes=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 2), dtype=torch.uint8, device=dev),
         k_meta=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 32, 2), dtype=torch.float16, device=dev),
         page_minmax=(torch.zeros((s.B, s.Hkv, w.max_pages, 2, s.d), dtype=torch.float16,
-                                 device=dev) if with_bounds else None))
+                                 device=dev) if with_bounds else None),
+        last_token=torch.from_numpy(np.maximum(w.seq_lens.astype(np.int32) - 1, 0)).to(dev))
 
 
 @dataclasses.dataclass
@@ -128,10 +137,14 @@ def alloc_step(c: DeviceCache) -> StepBuffers:
 
 
 def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[float] = None,
-             stream=None, stages=("select", "estimate", "topp", "decode")) -> None:
-    """One decode step of the hot path on `stream` (no host synchronization)."""
+             stream=None, stages=("select", "estimate", "topp", "decode"),
+             append: bool = False) -> None:
+    """One decode step of the hot path on `stream` (no host synchronization). With
+    append, the step first maintains the caches for each sequence's newest token."""
     if sm_scale is None:
         sm_scale = default_sm_scale(c.d)
+    if append:
+        c.append_last_token(stream=stream)
     lay = c.layout()
     stride = c.cand_stride_pages
     if c.budget is not None and "select" in stages:

@@ -174,6 +174,49 @@ def time_baselines(reps, bufs, stream, steps, warmup, twilight_us):
     return out
 
 
+def time_append_and_layers(reps, bufs, p, stream, steps, warmup, layers=32):
+    """Two views of a real decode loop, hipGraph replays: the step with its per-token cache
+    maintenance first (quantize the newest token, recompute its page's bounds), and one
+    graph of `layers` such steps over the rotating replicas (a whole model's attention
+    layers), reported per layer."""
+    import torch
+    from adaptive_top_sparse_amd import pipeline
+    R = len(reps)
+    graphs = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            pipeline.run_step(reps[r], bufs[r], p, stream=stream, append=True)
+        graphs.append(g)
+    big = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(big, stream=stream):
+        for i in range(layers):
+            pipeline.run_step(reps[i % R], bufs[i % R], p, stream=stream, append=True)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            graphs[i % R].replay()
+        big.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            graphs[i % R].replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / steps * 1e3
+    n_big = max(1, steps // layers)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(n_big):
+            big.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    layer_us = e0.elapsed_time(e1) / (n_big * layers) * 1e3
+    return {"append_step_us": step_us, "layers": layers,
+            "whole_model_graph_us_per_layer": layer_us}
+
+
 def cpu_baseline(w, p, seconds):
     """The fp64 oracle (stages select, estimate, top-p, attention; the cache is quantized
     beforehand, as on the GPU) on whole decode steps of the same workload, single thread,
@@ -348,12 +391,17 @@ def main():
         "cache_build_ms": build_ms,
         "roofline": roofline,
         "baselines": None,
+        "decode_loop": None,
         "cpu_baseline": None,
     }
     if not args.no_baselines:
         print("[bench] timing the dense and Quest-only steps", file=sys.stderr, flush=True)
         res["baselines"] = time_baselines(reps, bufs, stream, args.steps, args.warmup,
                                           graph_ms * 1e3)
+        print("[bench] timing the step with per-token cache maintenance", file=sys.stderr,
+              flush=True)
+        res["decode_loop"] = time_append_and_layers(reps, bufs, p, stream, args.steps,
+                                                    args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, p, args.cpu_seconds)

@@ -97,6 +97,18 @@ int twilight_quantize_keys(const twl_layout_t* L, const void* k_cache,
 int quest_page_bounds(const twl_layout_t* L, const void* k_cache,
                       const int32_t* token_begin, void* page_minmax, hipStream_t stream);
 
+/* Per-step cache maintenance for a decode loop (the pages' setting is decode with a KV
+ * cache that grows by one token per step, atlas.scime.ai "Approach"): for every sequence,
+ * the int4 codes of tokens [token_begin[b], seq_len_b), exactly as twilight_quantize_keys
+ * writes them, and, when page_minmax is not NULL, the bounds of every page holding such a
+ * token, exactly as quest_page_bounds writes them. One launch of one wave per (sequence, KV
+ * head) that reads each touched page's rows once, for an append of a few tokens per step.
+ * token_begin (device, int32[B]) is required; values below 0 mean 0. k_cache, k_codes and
+ * page_minmax must be 16-byte aligned, token_begin and k_meta 4-byte aligned; otherwise
+ * TWL_ERR_INVALID_ARG and nothing is enqueued. The caller owns every buffer. */
+int twilight_append_keys(const twl_layout_t* L, const void* k_cache, const int32_t* token_begin,
+                         uint8_t* k_codes, void* k_meta, void* page_minmax, hipStream_t stream);
+
 /* Quest base selector, the first (page-level top-k) stage of the hierarchy (atlas.scime.ai
  * "Approach" and "Surprising findings"). score(page) = sum over the KV head's G query heads
  * h and channels c of max(q_hc * min_c, q_hc * max_c), the largest value of q_h . k over

@@ -214,3 +214,157 @@ def test_host_errors_enqueue_nothing():
     assert e.value.status == twl.TWL_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert torch.all(buf.out == 7).item() and torch.all(buf.kept_count == 5).item()
+
+
+def test_step_with_append_matches_prebuilt_caches():
+    pl = _pipeline()
+    print("\n[edge] step with per-token cache maintenance", flush=True)
+    w = workloads.make_workload(3, n=4096 + 7, budget=64)
+    c = pl.upload(w)
+    c.build_caches()
+    buf = pl.alloc_step(c)
+    pl.run_step(c, buf, 0.9)
+    torch.cuda.synchronize()
+    plain = _host(buf)
+    codes0, meta0, mm0 = c.k_codes.clone(), c.k_meta.clone(), c.page_minmax.clone()
+    pl.run_step(c, buf, 0.9, append=True)
+    torch.cuda.synchronize()
+    appended = _host(buf)
+    assert torch.equal(codes0, c.k_codes) and torch.equal(meta0, c.k_meta)
+    assert torch.equal(mm0, c.page_minmax)
+    for key in ("sel_pages", "sel_count", "weights", "kept_count", "tau", "out"):
+        assert np.array_equal(plain[key].view(np.uint8), appended[key].view(np.uint8)), key
+
+
+@pytest.mark.parametrize("form", ["separate", "fused", "fused-codes-only"])
+@pytest.mark.parametrize("back", [1, 40])
+@pytest.mark.parametrize("d", [128, 64])
+def test_append_over_several_pages_equals_a_full_rebuild(back, form, d):
+    pl = _pipeline()
+    print(f"\n[edge] append of the last {back} tokens, {form}, d={d}", flush=True)
+    w = workloads.make_workload(4, B=3, seq_lens=[300, 1000, 37], budget=8, Hq=4, Hkv=4, d=d)
+    c = pl.upload(w)
+    c.build_caches()
+    full = (c.k_codes.clone(), c.k_meta.clone(), c.page_minmax.clone())
+    # wipe everything, then rebuild only from `back` tokens before the end of each sequence:
+    # rows before that point keep the wiped value, rows after must match the full rebuild
+    c.k_codes.fill_(0xAB)
+    c.k_meta.fill_(7)
+    c.page_minmax.fill_(3)
+    begin = torch.from_numpy(np.maximum(w.seq_lens.astype(np.int32) - back, 0)).cuda()
+    lay = c.layout()
+    if form == "separate":
+        twl.twilight_quantize_keys(lay, c.k_cache, c.k_codes, c.k_meta, token_begin=begin)
+        twl.quest_page_bounds(lay, c.k_cache, c.page_minmax, token_begin=begin)
+    else:
+        twl.twilight_append_keys(lay, c.k_cache, begin, c.k_codes, c.k_meta,
+                                 c.page_minmax if form == "fused" else None)
+    torch.cuda.synchronize()
+    codes_h, meta_h, mm_h = c.k_codes.cpu().numpy(), c.k_meta.cpu().numpy(), c.page_minmax.cpu().numpy()
+    fc, fm, fb = (t.cpu().numpy() for t in full)
+    for b in range(3):
+        n = int(w.seq_lens[b])
+        b0 = max(n - back, 0)
+        for t in range(n):
+            phys = w.page_table[b, t // 16]
+            got = codes_h[phys, :, t % 16]
+            if t >= b0:
+                assert np.array_equal(got, fc[phys, :, t % 16]), (b, t)
+                assert np.array_equal(meta_h[phys, :, t % 16].view(np.uint16),
+                                      fm[phys, :, t % 16].view(np.uint16)), (b, t)
+            else:
+                assert np.all(got == 0xAB), (b, t)
+        for page in range(-(-n // 16)):
+            if form != "fused-codes-only" and (page + 1) * 16 > b0:
+                assert np.array_equal(mm_h[b, :, page].view(np.uint16),
+                                      fb[b, :, page].view(np.uint16)), (b, page)
+            else:
+                assert np.all(mm_h[b, :, page].view(np.uint16) == np.float16(3).view(np.uint16))
+
+
+def test_append_keys_rejects_bad_arguments():
+    pl = _pipeline()
+    w = workloads.make_workload(4, B=1, seq_lens=[40], budget=8, Hq=4, Hkv=4)
+    c = pl.upload(w)
+    lay = c.layout()
+    with pytest.raises(twl.TwilightError) as e:
+        twl.twilight_append_keys(lay, c.k_cache, None, c.k_codes, c.k_meta, c.page_minmax)
+    assert e.value.status == twl.TWL_ERR_INVALID_ARG
+
+
+def _crafted_group(kind: int, rng) -> np.ndarray:
+    """32 fp16 bit patterns that stress the quantizer's tie rules."""
+    f16 = lambda a: np.asarray(a, np.float16).view(np.uint16)
+    if kind == 0:                                  # constant: scale 0, every code 0
+        return f16(np.full(32, 1.25))
+    if kind == 1:                                  # only zeros, -0 first: zero keeps -0
+        z = f16(np.zeros(32))
+        z[0::2] = 0x8000
+        return z
+    if kind == 2:                                  # tied minimum -1.5 at channels 7 and 20
+        x = rng.uniform(-1.0, 1.0, 32).astype(np.float16)
+        x[7] = x[20] = -1.5
+        return f16(x)
+    if kind == 3:                                  # +0 at 3 before -0 at 5, rest positive
+        x = rng.uniform(0.25, 2.0, 32).astype(np.float16)
+        x[3], x[5] = 0.0, -0.0
+        return f16(x)
+    if kind == 4:                                  # the widest finite range
+        x = rng.uniform(-1.0, 1.0, 32).astype(np.float16)
+        x[0], x[31] = -65504.0, 65504.0
+        return f16(x)
+    if kind == 5:                                  # subnormals only
+        return (rng.integers(0, 1024, 32) | (rng.integers(0, 2, 32) << 15)).astype(np.uint16)
+    # exact half-integer quotients: zero 0, scale 1, values k/2 -> ties to the even code
+    x = (np.arange(32) % 31 / 2.0).astype(np.float16)
+    x[1] = 15.0
+    return f16(x)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_append_keys_tie_rules_match_oracle(d):
+    pl = _pipeline()
+    print(f"\n[edge] append quantizer tie rules, d={d}", flush=True)
+    w = workloads.make_workload(4, B=2, seq_lens=[77, 260], budget=8, Hq=4, Hkv=4, d=d)
+    rng = np.random.default_rng(11)
+    c = pl.upload(w)
+    kh = c.k_cache.cpu().numpy().view(np.uint16).copy()           # [P, Hkv, 16, d]
+    back = 40
+    for b in range(2):
+        n = int(w.seq_lens[b])
+        for t in range(n - back, n):
+            phys = w.page_table[b, t // 16]
+            for kvh in range(4):
+                kh[phys, kvh, t % 16] = np.concatenate(
+                    [_crafted_group((t + kvh + g) % 7, rng) for g in range(d // 32)])
+    c.k_cache.copy_(torch.from_numpy(kh.view(np.float16)).to(c.k_cache.device))
+    c.build_caches()
+    full = (c.k_codes.cpu().numpy(), c.k_meta.cpu().numpy().view(np.uint16),
+            c.page_minmax.cpu().numpy().view(np.uint16))
+    c.k_codes.fill_(0xAB)
+    c.k_meta.fill_(7)
+    c.page_minmax.fill_(3)
+    begin = torch.from_numpy(np.maximum(w.seq_lens.astype(np.int32) - back, 0)).cuda()
+    twl.twilight_append_keys(c.layout(), c.k_cache, begin, c.k_codes, c.k_meta, c.page_minmax)
+    torch.cuda.synchronize()
+    codes_h = c.k_codes.cpu().numpy()
+    meta_h = c.k_meta.cpu().numpy().view(np.uint16)
+    mm_h = c.page_minmax.cpu().numpy().view(np.uint16)
+    for b in range(2):
+        n = int(w.seq_lens[b])
+        pt = w.page_table[b]
+        for kvh in range(4):
+            rows = parity.logical_rows(kh, pt, n, kvh)[n - back:]
+            o_codes, o_scale, o_zero = oracle.quantize_keys(rows.view(np.float16))
+            got_codes = parity.logical_rows(codes_h, pt, n, kvh)[n - back:]
+            got_meta = parity.logical_rows(meta_h, pt, n, kvh)[n - back:]
+            assert np.array_equal(parity.unpack_codes(got_codes), o_codes), (b, kvh)
+            assert np.array_equal(got_meta[..., 0], o_scale.view(np.uint16)), (b, kvh)
+            assert np.array_equal(got_meta[..., 1], o_zero.view(np.uint16)), (b, kvh)
+            assert np.array_equal(got_codes, parity.logical_rows(full[0], pt, n, kvh)[n - back:])
+            assert np.array_equal(got_meta, parity.logical_rows(full[1], pt, n, kvh)[n - back:])
+            lo, hi = oracle.page_bounds(parity.logical_rows(kh, pt, n, kvh).view(np.float16))
+            for page in range((n - back) // 16, -(-n // 16)):
+                assert np.array_equal(mm_h[b, kvh, page, 0], lo[page].view(np.uint16)), (b, kvh, page)
+                assert np.array_equal(mm_h[b, kvh, page, 1], hi[page].view(np.uint16)), (b, kvh, page)
+                assert np.array_equal(mm_h[b, kvh, page], full[2][b, kvh, page])
