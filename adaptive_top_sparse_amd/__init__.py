@@ -26,7 +26,9 @@ TWL_ERR_LAUNCH = -4
 
 EXPORTED = ("twilight_quantize_keys", "quest_page_bounds", "quest_select_pages",
             "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode",
-            "twilight_append_keys", "twilight_workspace_size", "twilight_status_string")
+            "twilight_append_keys", "twilight_topp_select_headwise",
+            "twilight_sparse_decode_headwise", "twilight_workspace_size",
+            "twilight_status_string")
 
 
 class TwilightError(RuntimeError):
@@ -64,7 +66,9 @@ def lib():
         L.twilight_topp_select.argtypes = [LP, P, P, P, I32, F, P, P, P, P, SZ, P]
         L.twilight_sparse_decode.argtypes = [LP, P, P, P, P, P, I32, F, P, P, SZ, P]
         L.twilight_append_keys.argtypes = [LP, P, P, P, P, P, P]
-        for name in EXPORTED[:7]:
+        L.twilight_topp_select_headwise.argtypes = L.twilight_topp_select.argtypes
+        L.twilight_sparse_decode_headwise.argtypes = L.twilight_sparse_decode.argtypes
+        for name in EXPORTED[:9]:
             getattr(L, name).restype = ctypes.c_int
         L.twilight_workspace_size.argtypes = [LP, I32]
         L.twilight_workspace_size.restype = ctypes.c_size_t
@@ -185,11 +189,11 @@ def twilight_estimate_weights(layout: Layout, q, k_codes, k_meta, cand_pages, ca
     _check("twilight_estimate_weights", st)
 
 
-def twilight_topp_select(layout: Layout, weights, cand_pages, cand_count,
-                         cand_stride_pages: int, p: float, kept, kept_count, tau, workspace,
-                         stream=None) -> None:
+def _topp_select(name: str, layout: Layout, weights, cand_pages, cand_count,
+                 cand_stride_pages: int, p: float, kept, kept_count, tau, workspace,
+                 stream=None) -> None:
     import torch
-    st = lib().twilight_topp_select(
+    st = getattr(lib(), name)(
         ctypes.byref(layout), _ptr(weights, torch.float32, "weights"),
         _ptr(cand_pages, torch.int32, "cand_pages"), _ptr(cand_count, torch.int32, "cand_count"),
         int(cand_stride_pages), float(p), _ptr(kept, torch.int32, "kept"),
@@ -197,17 +201,48 @@ def twilight_topp_select(layout: Layout, weights, cand_pages, cand_count,
         _ptr(workspace, None, "workspace"),
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream))
-    _check("twilight_topp_select", st)
+    _check(name, st)
 
 
-def twilight_sparse_decode(layout: Layout, q, k_cache, v_cache, kept, kept_count,
-                           kept_stride: int, sm_scale: float, out, workspace,
-                           stream=None) -> None:
+def twilight_topp_select(layout: Layout, weights, cand_pages, cand_count,
+                         cand_stride_pages: int, p: float, kept, kept_count, tau, workspace,
+                         stream=None) -> None:
+    """Group-wise: kept [B, Hkv, stride * 16], kept_count and tau [B, Hkv]."""
+    _topp_select("twilight_topp_select", layout, weights, cand_pages, cand_count,
+                 cand_stride_pages, p, kept, kept_count, tau, workspace, stream)
+
+
+def twilight_topp_select_headwise(layout: Layout, weights, cand_pages, cand_count,
+                                  cand_stride_pages: int, p: float, kept, kept_count, tau,
+                                  workspace, stream=None) -> None:
+    """Head-wise: kept [B, Hq, stride * 16], kept_count and tau [B, Hq]."""
+    _topp_select("twilight_topp_select_headwise", layout, weights, cand_pages, cand_count,
+                 cand_stride_pages, p, kept, kept_count, tau, workspace, stream)
+
+
+def _sparse_decode(name: str, layout: Layout, q, k_cache, v_cache, kept, kept_count,
+                   kept_stride: int, sm_scale: float, out, workspace, stream=None) -> None:
     import torch
-    st = lib().twilight_sparse_decode(
+    st = getattr(lib(), name)(
         ctypes.byref(layout), _ptr(q, torch.float16, "q"), _ptr(k_cache, torch.float16, "k_cache"),
         _ptr(v_cache, torch.float16, "v_cache"), _ptr(kept, torch.int32, "kept"),
         _ptr(kept_count, torch.int32, "kept_count"), int(kept_stride), float(sm_scale),
         _ptr(out, torch.float16, "out"), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("twilight_sparse_decode", st)
+    _check(name, st)
+
+
+def twilight_sparse_decode(layout: Layout, q, k_cache, v_cache, kept, kept_count,
+                           kept_stride: int, sm_scale: float, out, workspace,
+                           stream=None) -> None:
+    """Group-wise kept lists [B, Hkv, kept_stride]."""
+    _sparse_decode("twilight_sparse_decode", layout, q, k_cache, v_cache, kept, kept_count,
+                   kept_stride, sm_scale, out, workspace, stream)
+
+
+def twilight_sparse_decode_headwise(layout: Layout, q, k_cache, v_cache, kept, kept_count,
+                                    kept_stride: int, sm_scale: float, out, workspace,
+                                    stream=None) -> None:
+    """Head-wise kept lists [B, Hq, kept_stride]."""
+    _sparse_decode("twilight_sparse_decode_headwise", layout, q, k_cache, v_cache, kept,
+                   kept_count, kept_stride, sm_scale, out, workspace, stream)

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ kept,
-    const int32_t* __restrict__ kept_count, int kept_stride, int Hkv, int max_pages,
+    const int32_t* __restrict__ kept_count, int kept_stride, int units, int Hkv, int max_pages,
     int num_phys, float scale_log2, float* __restrict__ part_o, float2* __restrict__ part_ml,
     int n_chunks, int chunk_tokens, uint16_t* __restrict__ out) {
   constexpr int LPT = D / 8;        // lanes per token row
@@ -85,11 +85,14 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   // work-groups are numbered chunk-major (every KV head's first chunk, then every second
   // chunk, ...), so that chunks past a short kept list, which exit at once, are dispatched
   // last instead of holding slots ahead of useful work
+  // a unit is a KV head and its G query heads, or (head-wise, G = 1) one query head, whose
+  // K/V rows are those of KV head g / (units / Hkv)
   const int b = blockIdx.y;
-  const int g = blockIdx.x % Hkv;
-  const int chunk = blockIdx.x / Hkv;
-  const long unit = static_cast<long>(b) * Hkv + g;
-  const int Hq = Hkv * G;
+  const int g = blockIdx.x % units;
+  const int chunk = blockIdx.x / units;
+  const long unit = static_cast<long>(b) * units + g;
+  const int kvh = g / (units / Hkv);
+  const int Hq = units * G;
   const long head0 = static_cast<long>(b) * Hq + g * G;
   const int t0 = chunk * chunk_tokens;
   const int tend = min(kept_stride, t0 + chunk_tokens);  // the chunk's slots in the list
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   };
   auto row_of = [&](int phys, int tok) -> long {
     if (tok < 0 || !phys_ok(phys, num_phys)) return -1;
-    return ((static_cast<long>(phys) * Hkv + g) * kPage + tok % kPage) * D;
+    return ((static_cast<long>(phys) * Hkv + kvh) * kPage + tok % kPage) * D;
   };
   auto load_kv = [&](const int (&phys)[U], const int (&tok)[U], bool (&live)[U],
                      u32x4 (&kv)[U], u32x4 (&vv)[U]) {
@@ -338,14 +341,14 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 template <int D>
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-    const int32_t* __restrict__ kept_count, int kept_stride, int Hkv, int G, int n_chunks,
+    const int32_t* __restrict__ kept_count, int kept_stride, int units, int G, int n_chunks,
     int chunk_tokens, uint16_t* __restrict__ out) {
   __shared__ float s_acc[kWave][kMergeSlice + 1];
   const int slice = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int Hq = Hkv * G;
-  const long unit = static_cast<long>(b) * Hkv + h / G;
+  const int Hq = units * G;
+  const long unit = static_cast<long>(b) * units + h / G;
   int K = kept_count[unit];
   K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
   const int nc = (K + chunk_tokens - 1) / chunk_tokens;
@@ -393,10 +396,10 @@ void decode_launch(const Layout& L, const void* q, const void* k, const void* v,
                    const int32_t* kept, const int32_t* kept_count, int kept_stride,
                    float scale_log2, float* part_o, float2* part_ml, int n_chunks, int ch,
                    void* out, hipStream_t s) {
-  sparse_decode_kernel<D, G><<<dim3(n_chunks * L.Hkv, L.B), kDecThreads, 0, s>>>(
+  sparse_decode_kernel<D, G><<<dim3(n_chunks * L.units(), L.B), kDecThreads, 0, s>>>(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), L.page_table, L.seq_lens, kept, kept_count, kept_stride,
-      L.Hkv, L.max_pages, L.num_phys, scale_log2, part_o, part_ml, n_chunks, ch,
+      L.units(), L.Hkv, L.max_pages, L.num_phys, scale_log2, part_o, part_ml, n_chunks, ch,
       static_cast<uint16_t*>(out));
 }
 
@@ -405,7 +408,7 @@ void decode_dispatch_g(const Layout& L, const void* q, const void* k, const void
                        const int32_t* kept, const int32_t* kept_count, int kept_stride,
                        float scale_log2, float* part_o, float2* part_ml, int n_chunks, int ch,
                        void* out, hipStream_t s) {
-  switch (L.G()) {
+  switch (L.unit_G()) {
     case 1: decode_launch<D, 1>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, part_o, part_ml, n_chunks, ch, out, s); break;
     case 2: decode_launch<D, 2>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, part_o, part_ml, n_chunks, ch, out, s); break;
     case 4: decode_launch<D, 4>(L, q, k, v, kept, kept_count, kept_stride, scale_log2, part_o, part_ml, n_chunks, ch, out, s); break;
@@ -418,7 +421,7 @@ void decode_dispatch_g(const Layout& L, const void* q, const void* k, const void
 int decode_chunk_tokens(const Layout& L, int kept_stride) {
   // about TWL_DEC_TARGET_BLOCKS work-groups over the largest possible kept lists: one to
   // TWL_DEC_MAX_BATCHES batches per work-group
-  const long units = static_cast<long>(L.B) * L.Hkv;
+  const long units = static_cast<long>(L.B) * L.units();
   const long want =
       (static_cast<long>(kept_stride) * units + TWL_DEC_TARGET_BLOCKS - 1) / TWL_DEC_TARGET_BLOCKS;
   const int batch = decode_batch_tokens(L.d);
@@ -455,11 +458,11 @@ hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_ca
   auto* o = static_cast<uint16_t*>(out);
   const dim3 grid(L.d / kMergeSlice, L.Hq, L.B);
   if (L.d == 128) {
-    decode_merge_kernel<128><<<grid, kWave, 0, s>>>(part_o, part_ml, kept_count, kept_stride, L.Hkv,
-                                                    L.G(), n_chunks, ch, o);
+    decode_merge_kernel<128><<<grid, kWave, 0, s>>>(part_o, part_ml, kept_count, kept_stride,
+                                                    L.units(), L.unit_G(), n_chunks, ch, o);
   } else {
-    decode_merge_kernel<64><<<grid, kWave, 0, s>>>(part_o, part_ml, kept_count, kept_stride, L.Hkv,
-                                                   L.G(), n_chunks, ch, o);
+    decode_merge_kernel<64><<<grid, kWave, 0, s>>>(part_o, part_ml, kept_count, kept_stride,
+                                                    L.units(), L.unit_G(), n_chunks, ch, o);
   }
   return hipGetLastError();
 }

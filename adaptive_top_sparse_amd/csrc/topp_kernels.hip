@@ -169,7 +169,7 @@ template <int NT, int G, int SPT>
 __global__ __launch_bounds__(NT) void topp_kernel(
     const float* __restrict__ src, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages,
-    const int32_t* __restrict__ seq_lens, int Hkv, int max_pages, float p,
+    const int32_t* __restrict__ seq_lens, int units, int cand_div, int max_pages, float p,
     int32_t* __restrict__ kept, int32_t* __restrict__ kept_count,
     float* __restrict__ tau_out) {
   using M = SlotMap<NT, SPT>;
@@ -188,11 +188,13 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   TWL_PHASE(0);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
-  const long unit = static_cast<long>(b) * Hkv + g;
+  const long unit = static_cast<long>(b) * units + g;
+  // a head-wise unit (one query head) reads its KV head's candidates: cand_div = G
+  const long cunit = unit / cand_div;
   const int n = seq_len_clamped(seq_lens, b, max_pages);
   const int n_slots = cand_stride_pages * kPage;
-  const int32_t* cand_row = cand_pages ? cand_pages + unit * cand_stride_pages : nullptr;
-  const int cnt = candidate_pages(cand_pages, cand_count, unit, cand_stride_pages, n);
+  const int32_t* cand_row = cand_pages ? cand_pages + cunit * cand_stride_pages : nullptr;
+  const int cnt = candidate_pages(cand_pages, cand_count, cunit, cand_stride_pages, n);
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
   const int wbase = wv * SPT * kWave;
@@ -435,9 +437,9 @@ struct ToppArgs {
 
 template <int NT, int G, int SPT>
 void launch_main(const ToppArgs& a, const float* src) {
-  topp_kernel<NT, G, SPT><<<dim3(a.L->Hkv, a.L->B), NT, 0, a.s>>>(
-      src, a.cand_pages, a.cand_count, a.stride, a.L->seq_lens, a.L->Hkv, a.L->max_pages, a.p,
-      a.kept, a.kept_count, a.tau);
+  topp_kernel<NT, G, SPT><<<dim3(a.L->units(), a.L->B), NT, 0, a.s>>>(
+      src, a.cand_pages, a.cand_count, a.stride, a.L->seq_lens, a.L->units(),
+      a.L->headwise ? a.L->G() : 1, a.L->max_pages, a.p, a.kept, a.kept_count, a.tau);
 }
 
 template <int G>
@@ -466,7 +468,7 @@ bool uses_mean_pass(int G, int n_slots) {
 
 template <int NT, int SPT>
 void launch_spt(const ToppArgs& a) {
-  const int G = a.L->G();
+  const int G = a.L->unit_G();
   if (uses_mean_pass(G, a.stride * kPage)) {
     if (G == 2) launch_mean<2>(a);
     else if (G == 4) launch_mean<4>(a);
@@ -490,7 +492,7 @@ void launch_spt(const ToppArgs& a) {
 
 size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages) {
   const long n_slots = static_cast<long>(cand_stride_pages) * kPage;
-  if (!uses_mean_pass(L.G(), static_cast<int>(n_slots))) return 0;
+  if (!uses_mean_pass(L.unit_G(), static_cast<int>(n_slots))) return 0;
   return align_up(static_cast<size_t>(L.B) * L.Hkv * n_slots * sizeof(float), 256);
 }
 

@@ -46,7 +46,7 @@ int check_layout(const twl_layout_t* L, Layout* out, bool* empty) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_ERR_LAUNCH; }
 
-size_t workspace_for(const Layout& L, int cand_stride_pages) {
+size_t workspace_mode(const Layout& L, int cand_stride_pages) {
   size_t need = twl::quest_workspace_bytes(L);
   const size_t e = twl::estimate_workspace_bytes(L, cand_stride_pages);
   const size_t d = twl::decode_workspace_bytes(L, cand_stride_pages * twl::kPage);
@@ -55,6 +55,67 @@ size_t workspace_for(const Layout& L, int cand_stride_pages) {
   if (t > need) need = t;
   if (d > need) need = d;
   return need;
+}
+
+// Large enough for every call in either mode (group-wise or head-wise units).
+size_t workspace_for(Layout L, int cand_stride_pages) {
+  L.headwise = false;
+  const size_t group = workspace_mode(L, cand_stride_pages);
+  L.headwise = true;
+  const size_t head = workspace_mode(L, cand_stride_pages);
+  return group > head ? group : head;
+}
+
+int topp_select(bool headwise, const twl_layout_t* L, const float* weights,
+                const int32_t* cand_pages, const int32_t* cand_count, int32_t cand_stride_pages,
+                float p, int32_t* kept, int32_t* kept_count, float* tau, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  Layout lay{};
+  bool empty = false;
+  int st = check_layout(L, &lay, &empty);
+  if (st != TWL_OK) return st;
+  lay.headwise = headwise;
+  if (weights == nullptr || kept == nullptr || kept_count == nullptr) return TWL_ERR_INVALID_ARG;
+  if (!aligned16(weights) || !aligned4(kept) || !aligned4(kept_count)) return TWL_ERR_INVALID_ARG;
+  if (cand_pages != nullptr && !aligned4(cand_pages)) return TWL_ERR_INVALID_ARG;
+  if (cand_count != nullptr && !aligned4(cand_count)) return TWL_ERR_INVALID_ARG;
+  if (tau != nullptr && !aligned4(tau)) return TWL_ERR_INVALID_ARG;
+  if (cand_stride_pages < 1 || !(p > 0.0f && p <= 1.0f)) return TWL_ERR_INVALID_ARG;
+  if (cand_pages == nullptr && cand_stride_pages < lay.max_pages) return TWL_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(cand_stride_pages) * twl::kPage > twl::kToppMaxSlots)
+    return TWL_ERR_UNSUPPORTED;
+  if (empty) return TWL_OK;
+  const size_t need = twl::topp_workspace_bytes(lay, cand_stride_pages);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) ||
+                   workspace_bytes < need))
+    return TWL_ERR_WORKSPACE;
+  return launch_status(twl::launch_topp(lay, weights, cand_pages, cand_count, cand_stride_pages,
+                                        p, kept, kept_count, tau, workspace, stream));
+}
+
+int sparse_decode(bool headwise, const twl_layout_t* L, const void* q, const void* k_cache,
+                  const void* v_cache, const int32_t* kept, const int32_t* kept_count,
+                  int32_t kept_stride, float sm_scale, void* out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  Layout lay{};
+  bool empty = false;
+  int st = check_layout(L, &lay, &empty);
+  if (st != TWL_OK) return st;
+  lay.headwise = headwise;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || kept == nullptr ||
+      kept_count == nullptr || out == nullptr)
+    return TWL_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(kept) ||
+      !aligned4(kept_count) || !aligned4(out))
+    return TWL_ERR_INVALID_ARG;
+  if (kept_stride < 1 || !std::isfinite(sm_scale)) return TWL_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(kept_stride) > twl::kToppMaxSlots * 64) return TWL_ERR_UNSUPPORTED;
+  if (empty) return TWL_OK;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < twl::decode_workspace_bytes(lay, kept_stride))
+    return TWL_ERR_WORKSPACE;
+  return launch_status(twl::launch_sparse_decode(lay, q, k_cache, v_cache, kept, kept_count,
+                                                 kept_stride, sm_scale, out, workspace, stream));
 }
 
 }  // namespace
@@ -177,50 +238,34 @@ int twilight_topp_select(const twl_layout_t* L, const float* weights, const int3
                          const int32_t* cand_count, int32_t cand_stride_pages, float p,
                          int32_t* kept, int32_t* kept_count, float* tau, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  Layout lay{};
-  bool empty = false;
-  int st = check_layout(L, &lay, &empty);
-  if (st != TWL_OK) return st;
-  if (weights == nullptr || kept == nullptr || kept_count == nullptr) return TWL_ERR_INVALID_ARG;
-  if (!aligned16(weights) || !aligned4(kept) || !aligned4(kept_count)) return TWL_ERR_INVALID_ARG;
-  if (cand_pages != nullptr && !aligned4(cand_pages)) return TWL_ERR_INVALID_ARG;
-  if (cand_count != nullptr && !aligned4(cand_count)) return TWL_ERR_INVALID_ARG;
-  if (tau != nullptr && !aligned4(tau)) return TWL_ERR_INVALID_ARG;
-  if (cand_stride_pages < 1 || !(p > 0.0f && p <= 1.0f)) return TWL_ERR_INVALID_ARG;
-  if (cand_pages == nullptr && cand_stride_pages < lay.max_pages) return TWL_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(cand_stride_pages) * twl::kPage > twl::kToppMaxSlots)
-    return TWL_ERR_UNSUPPORTED;
-  if (empty) return TWL_OK;
-  const size_t need = twl::topp_workspace_bytes(lay, cand_stride_pages);
-  if (need > 0 && (workspace == nullptr || !aligned16(workspace) ||
-                   workspace_bytes < need))
-    return TWL_ERR_WORKSPACE;
-  return launch_status(twl::launch_topp(lay, weights, cand_pages, cand_count, cand_stride_pages,
-                                        p, kept, kept_count, tau, workspace, stream));
+  return topp_select(false, L, weights, cand_pages, cand_count, cand_stride_pages, p, kept,
+                     kept_count, tau, workspace, workspace_bytes, stream);
+}
+
+int twilight_topp_select_headwise(const twl_layout_t* L, const float* weights,
+                                  const int32_t* cand_pages, const int32_t* cand_count,
+                                  int32_t cand_stride_pages, float p, int32_t* kept,
+                                  int32_t* kept_count, float* tau, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return topp_select(true, L, weights, cand_pages, cand_count, cand_stride_pages, p, kept,
+                     kept_count, tau, workspace, workspace_bytes, stream);
 }
 
 int twilight_sparse_decode(const twl_layout_t* L, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* kept, const int32_t* kept_count,
                            int32_t kept_stride, float sm_scale, void* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-  Layout lay{};
-  bool empty = false;
-  int st = check_layout(L, &lay, &empty);
-  if (st != TWL_OK) return st;
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || kept == nullptr ||
-      kept_count == nullptr || out == nullptr)
-    return TWL_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(kept) ||
-      !aligned4(kept_count) || !aligned4(out))
-    return TWL_ERR_INVALID_ARG;
-  if (kept_stride < 1 || !std::isfinite(sm_scale)) return TWL_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(kept_stride) > twl::kToppMaxSlots * 64) return TWL_ERR_UNSUPPORTED;
-  if (empty) return TWL_OK;
-  if (workspace == nullptr || !aligned16(workspace) ||
-      workspace_bytes < twl::decode_workspace_bytes(lay, kept_stride))
-    return TWL_ERR_WORKSPACE;
-  return launch_status(twl::launch_sparse_decode(lay, q, k_cache, v_cache, kept, kept_count,
-                                                 kept_stride, sm_scale, out, workspace, stream));
+  return sparse_decode(false, L, q, k_cache, v_cache, kept, kept_count, kept_stride, sm_scale,
+                       out, workspace, workspace_bytes, stream);
+}
+
+int twilight_sparse_decode_headwise(const twl_layout_t* L, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* kept,
+                                    const int32_t* kept_count, int32_t kept_stride,
+                                    float sm_scale, void* out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  return sparse_decode(true, L, q, k_cache, v_cache, kept, kept_count, kept_stride, sm_scale,
+                       out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -17,7 +17,12 @@ struct Layout {
   int B, Hq, Hkv, d, max_pages, num_phys;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  // Top-p and decode units: one kept set per KV head, shared by its G query heads
+  // (group-wise), or one per query head (head-wise).
+  bool headwise = false;
   int G() const { return Hq / Hkv; }
+  int units() const { return headwise ? Hq : Hkv; }   // units per sequence
+  int unit_G() const { return headwise ? 1 : Hq / Hkv; }  // query heads per unit
 };
 
 // Rows of candidate slots are processed in chunks of this many slots by the estimate.

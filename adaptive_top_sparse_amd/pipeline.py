@@ -15,8 +15,9 @@ import numpy as np
 import torch
 
 from . import (PAGE_SIZE, make_layout, quest_page_bounds, quest_select_pages,
-               twilight_append_keys, twilight_estimate_weights, twilight_quantize_keys, twilight_sparse_decode,
-               twilight_topp_select, twilight_workspace_size)
+               twilight_append_keys, twilight_estimate_weights, twilight_quantize_keys,
+               twilight_sparse_decode, twilight_sparse_decode_headwise, twilight_topp_select,
+               twilight_topp_select_headwise, twilight_workspace_size)
 
 
 def default_sm_scale(d: int) -> float:
@@ -115,8 +116,10 @@ class StepBuffers:
     workspace: torch.Tensor
 
 
-def alloc_step(c: DeviceCache) -> StepBuffers:
+def alloc_step(c: DeviceCache, headwise: bool = False) -> StepBuffers:
+    """Step outputs; with headwise, the kept lists, counts and tau are per query head."""
     dev = c.q.device
+    H = c.Hq if headwise else c.Hkv
     stride = c.cand_stride_pages
     n_slots = stride * PAGE_SIZE
     ws_bytes = twilight_workspace_size(c.layout(), stride)
@@ -128,9 +131,9 @@ def alloc_step(c: DeviceCache) -> StepBuffers:
         sel_count=(torch.zeros((c.B, c.Hkv), dtype=torch.int32, device=dev)
                    if c.budget is not None else None),
         weights=torch.zeros((c.B, c.Hq, n_slots), dtype=torch.float32, device=dev),
-        kept=torch.full((c.B, c.Hkv, n_slots), -1, dtype=torch.int32, device=dev),
-        kept_count=torch.zeros((c.B, c.Hkv), dtype=torch.int32, device=dev),
-        tau=torch.zeros((c.B, c.Hkv), dtype=torch.float32, device=dev),
+        kept=torch.full((c.B, H, n_slots), -1, dtype=torch.int32, device=dev),
+        kept_count=torch.zeros((c.B, H), dtype=torch.int32, device=dev),
+        tau=torch.zeros((c.B, H), dtype=torch.float32, device=dev),
         out=torch.zeros((c.B, c.Hq, c.d), dtype=torch.float16, device=dev),
         # zero-filled once; the library needs no particular contents
         workspace=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev))
@@ -138,9 +141,11 @@ def alloc_step(c: DeviceCache) -> StepBuffers:
 
 def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[float] = None,
              stream=None, stages=("select", "estimate", "topp", "decode"),
-             append: bool = False) -> None:
+             append: bool = False, headwise: bool = False) -> None:
     """One decode step of the hot path on `stream` (no host synchronization). With
-    append, the step first maintains the caches for each sequence's newest token."""
+    append, the step first maintains the caches for each sequence's newest token; with
+    headwise (buffers from alloc_step(c, headwise=True)), top-p and decode keep one set per
+    query head instead of one per KV head."""
     if sm_scale is None:
         sm_scale = default_sm_scale(c.d)
     if append:
@@ -155,13 +160,14 @@ def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[floa
     if "estimate" in stages:
         twilight_estimate_weights(lay, c.q, c.k_codes, c.k_meta, cand_pages, cand_count, stride,
                                   sm_scale, buf.weights, buf.workspace, stream=stream)
+    topp = twilight_topp_select_headwise if headwise else twilight_topp_select
+    decode = twilight_sparse_decode_headwise if headwise else twilight_sparse_decode
     if "topp" in stages:
-        twilight_topp_select(lay, buf.weights, cand_pages, cand_count, stride, p, buf.kept,
-                             buf.kept_count, buf.tau, buf.workspace, stream=stream)
+        topp(lay, buf.weights, cand_pages, cand_count, stride, p, buf.kept, buf.kept_count,
+             buf.tau, buf.workspace, stream=stream)
     if "decode" in stages:
-        twilight_sparse_decode(lay, c.q, c.k_cache, c.v_cache, buf.kept, buf.kept_count,
-                               stride * PAGE_SIZE, sm_scale, buf.out, buf.workspace,
-                               stream=stream)
+        decode(lay, c.q, c.k_cache, c.v_cache, buf.kept, buf.kept_count, stride * PAGE_SIZE,
+               sm_scale, buf.out, buf.workspace, stream=stream)
 
 
 def baseline_kept(c: DeviceCache, buf: StepBuffers, mode: str):

@@ -217,6 +217,39 @@ def time_append_and_layers(reps, bufs, p, stream, steps, warmup, layers=32):
             "whole_model_graph_us_per_layer": layer_us}
 
 
+def time_headwise(reps, bufs, p, stream, steps, warmup):
+    """The step with head-wise top-p and decode (a kept set per query head instead of one per
+    KV-head group), hipGraph replays in rotation over the same replicas, with the kept
+    token-heads of both modes (a group-wise kept token counts once per query head)."""
+    import torch
+    from adaptive_top_sparse_amd import pipeline
+    hbufs = [pipeline.alloc_step(c, headwise=True) for c in reps]
+    graphs = []
+    for c, hb in zip(reps, hbufs):
+        with torch.cuda.stream(stream):
+            pipeline.run_step(c, hb, p, stream=stream, headwise=True)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            pipeline.run_step(c, hb, p, stream=stream, headwise=True)
+        graphs.append(g)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    G = reps[0].Hq // reps[0].Hkv
+    return {"headwise_step_us": e0.elapsed_time(e1) / steps * 1e3,
+            "kept_token_heads_headwise": int(hbufs[0].kept_count.sum().item()),
+            "kept_token_heads_groupwise": int(bufs[0].kept_count.sum().item()) * G}
+
+
 def cpu_baseline(w, p, seconds):
     """The fp64 oracle (stages select, estimate, top-p, attention; the cache is quantized
     beforehand, as on the GPU) on whole decode steps of the same workload, single thread,
@@ -392,6 +425,7 @@ def main():
         "roofline": roofline,
         "baselines": None,
         "decode_loop": None,
+        "headwise": None,
         "cpu_baseline": None,
     }
     if not args.no_baselines:
@@ -402,6 +436,9 @@ def main():
               flush=True)
         res["decode_loop"] = time_append_and_layers(reps, bufs, p, stream, args.steps,
                                                     args.warmup)
+        if reps[0].Hq != reps[0].Hkv:
+            print("[bench] timing the head-wise step", file=sys.stderr, flush=True)
+            res["headwise"] = time_headwise(reps, bufs, p, stream, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, p, args.cpu_seconds)

@@ -158,6 +158,20 @@ int twilight_topp_select(const twl_layout_t* L, const float* weights,
                          int32_t* kept_count, float* tau, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/* Head-wise top-p under GQA (atlas.scime.ai "Limitations": under GQA the pages' dynamic
+ * budgets are per group, not per head, which costs adaptivity; this is the per-head form).
+ * Each query head h is its own unit: the rule of twilight_topp_select with G = 1, applied to
+ * weights[h] over the candidates of its KV head h / G. Same arguments, except:
+ *   kept       : int32 [B, Hq, cand_stride_pages * 16]
+ *   kept_count : int32 [B, Hq]
+ *   tau        : fp32 [B, Hq] or NULL
+ * Needs no workspace; accepts the same workspace arguments. */
+int twilight_topp_select_headwise(const twl_layout_t* L, const float* weights,
+                                  const int32_t* cand_pages, const int32_t* cand_count,
+                                  int32_t cand_stride_pages, float p, int32_t* kept,
+                                  int32_t* kept_count, float* tau, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* Sparse paged decode attention over the kept tokens (atlas.scime.ai "Key results": the
  * Twilight sparse self-attention operator). For each query head h of KV head g:
  * o_h = sum_{j in kept} softmax_j(sm_scale * q_h . k_j) v_j over the fp16 K/V cache, the
@@ -170,6 +184,17 @@ int twilight_sparse_decode(const twl_layout_t* L, const void* q, const void* k_c
                            const void* v_cache, const int32_t* kept, const int32_t* kept_count,
                            int32_t kept_stride, float sm_scale, void* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* Sparse decode with one kept set per query head (the head-wise form above): o_h is the
+ * attention of q_h over its own kept tokens, whose K/V rows are those of KV head h / G.
+ * Same arguments as twilight_sparse_decode, except:
+ *   kept       : int32 [B, Hq, kept_stride] logical token ids
+ *   kept_count : int32 [B, Hq] (clamped to kept_stride) */
+int twilight_sparse_decode_headwise(const twl_layout_t* L, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* kept,
+                                    const int32_t* kept_count, int32_t kept_stride,
+                                    float sm_scale, void* out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes that every call above needs for this layout when candidate and kept
  * lists have cand_stride_pages pages (kept_stride = cand_stride_pages * 16). One

@@ -178,13 +178,20 @@ def nearest_half_of_ratio(num: float, den: int) -> int:
     return int(lib().orc_nearest_half_of_ratio(num, den))
 
 
-def run_unit(q_group, k, v, budget, p, sm_scale, page_size: int = 16):
+def run_unit(q_group, k, v, budget, p, sm_scale, page_size: int = 16,
+             headwise: bool = False):
     """Whole hot path for one (sequence, KV head) unit, stage by stage.
 
     q_group: [G, d] fp16 (the query heads sharing the KV head); k, v: [n, d] fp16 logical
     order; budget: Quest pages, or None when every token is a candidate. Returns a dict of
     every stage's output: codes/scale/zero, lo/hi, sel (ascending pages or None), weights
     [G, n_slots], valid [n_slots], kept (ascending token ids), tau, out [G, d] fp64.
+
+    headwise: top-p per query head instead of per group (the pages name the group-wise
+    budget under GQA as a limitation, atlas.scime.ai "Limitations"). Each head's kept set is
+    orc_topp_select with G = 1 on that head's own weights, over the same Quest candidates,
+    and its output is attention over its own kept set; kept is then a list of G arrays and
+    tau a list of G floats.
     """
     n = k.shape[0]
     codes, scale, zero = quantize_keys(k)
@@ -207,6 +214,13 @@ def run_unit(q_group, k, v, budget, p, sm_scale, page_size: int = 16):
     res["valid"] = valid
     w = estimate_weights(q_group, codes, scale, zero, n, sel, n_slots, sm_scale, page_size)
     res["weights"] = w
+    if headwise:
+        per = [topp_select(w[h:h + 1], valid, p, sel, page_size) for h in range(w.shape[0])]
+        res["kept"] = [kept for kept, _ in per]
+        res["tau"] = [tau for _, tau in per]
+        res["out"] = np.concatenate([sparse_attention(q_group[h:h + 1], k, v, per[h][0], sm_scale)
+                                     for h in range(w.shape[0])])
+        return res
     kept, tau = topp_select(w, valid, p, sel, page_size)
     res["kept"], res["tau"] = kept, tau
     res["out"] = sparse_attention(q_group, k, v, kept, sm_scale)

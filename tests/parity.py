@@ -43,7 +43,7 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
     return np.stack([lo, hi], axis=-1).reshape(packed.shape[0], -1)
 
 
-def oracle_units(w, p: float, units=None):
+def oracle_units(w, p: float, units=None, headwise: bool = False):
     """Oracle results per (b, kvh) unit (all units, or the listed ones)."""
     s = w.spec
     G = s.G
@@ -53,8 +53,15 @@ def oracle_units(w, p: float, units=None):
     res = {}
     for b, g in units:
         res[(b, g)] = oracle.run_unit(w.q[b, g * G:(g + 1) * G], w.k[b][g], w.v[b][g],
-                                      w.budget, p, sm)
+                                      w.budget, p, sm, headwise=headwise)
     return res
+
+
+def head_view(res, h: int):
+    """One query head of a head-wise oracle unit, shaped like a group-wise unit with G = 1
+    (for check_kept and check_out)."""
+    return {"weights": res["weights"][h:h + 1], "sel": res["sel"], "valid": res["valid"],
+            "kept": res["kept"][h], "tau": res["tau"][h], "out": res["out"][h:h + 1]}
 
 
 def slot_tokens(sel, n_slots: int, n: int) -> np.ndarray:

@@ -416,3 +416,53 @@ def test_attention_special_cases():
     sub = np.array([3, 9, 30], np.int32)
     a = oracle.sparse_attention(q, k, v, sub, 0.125)
     assert np.allclose(a, _dense_attention(q, k[sub], v[sub], 0.125), rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------- head-wise top-p under GQA (per query head) ---
+
+@pytest.mark.parametrize("trial", range(12))
+def test_headwise_unit_is_a_nucleus_and_attention_per_head(trial):
+    """Head-wise form: each query head's kept set is the minimal nucleus of its own weights
+    (brute force), its output is textbook attention over that set, and two heads planted on
+    different tokens keep their own planted token."""
+    G, d = 2, 64
+    n = int(RNG.integers(4, 12))
+    p = float(np.float32(RNG.uniform(0.3, 0.95)))
+    k = RNG.standard_normal((n, d)).astype(np.float16)
+    v = RNG.standard_normal((n, d)).astype(np.float16)
+    a, b = RNG.choice(n, 2, replace=False)
+    q = RNG.standard_normal((G, d)) * 0.3
+    q[0] += 0.8 * k[a].astype(np.float64)
+    q[1] += 0.8 * k[b].astype(np.float64)
+    q = q.astype(np.float16)
+    sm = float(np.float32(1 / math.sqrt(d)))
+    res = oracle.run_unit(q, k, v, None, p, sm, headwise=True)
+    assert len(res["kept"]) == G and res["out"].shape == (G, d)
+    for h, planted in ((0, a), (1, b)):
+        W = res["weights"][h, :n]
+        kept = res["kept"][h]
+        m_star, (mass_star, _) = _brute_force_min_nucleus(list(W), p)
+        assert len(kept) == m_star
+        assert math.isclose(W[kept].sum(), mass_star, rel_tol=1e-12)
+        assert res["tau"][h] == W[kept].min()
+        assert planted in kept
+        want = _dense_attention(q[h:h + 1], k[kept], v[kept], sm)
+        assert np.allclose(res["out"][h:h + 1], want, rtol=1e-12, atol=1e-14)
+    # the group-wise form on the same unit keeps the nucleus of the group mean instead
+    grp = oracle.run_unit(q, k, v, None, p, sm)
+    Wm = grp["weights"][:, :n].mean(0)
+    m_star, (mass_star, _) = _brute_force_min_nucleus(list(Wm), p)
+    assert len(grp["kept"]) == m_star
+
+
+def test_headwise_equals_groupwise_for_one_head_per_group():
+    d, n = 128, 70
+    k = RNG.standard_normal((n, d)).astype(np.float16)
+    v = RNG.standard_normal((n, d)).astype(np.float16)
+    q = RNG.standard_normal((1, d)).astype(np.float16)
+    sm = float(np.float32(1 / math.sqrt(d)))
+    for budget in (None, 2):
+        hw = oracle.run_unit(q, k, v, budget, 0.9, sm, headwise=True)
+        gw = oracle.run_unit(q, k, v, budget, 0.9, sm)
+        assert np.array_equal(hw["kept"][0], gw["kept"]) and hw["tau"][0] == gw["tau"]
+        assert np.array_equal(hw["out"], gw["out"])
