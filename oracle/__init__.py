@@ -33,6 +33,8 @@ def lib():
         L.orc_version.restype = c_int
         L.orc_quantize_keys.argtypes = [_u16p, i64, c_int, _u8p, _u16p, _u16p]
         L.orc_quantize_keys.restype = c_int
+        L.orc_quantize_keys_bits.argtypes = [_u16p, i64, c_int, c_int, _u8p, _u16p, _u16p]
+        L.orc_quantize_keys_bits.restype = c_int
         L.orc_page_bounds.argtypes = [_u16p, i64, c_int, c_int, _u16p, _u16p]
         L.orc_page_bounds.restype = c_int
         L.orc_quest_select.argtypes = [_u16p, c_int, c_int, _u16p, _u16p, i64, c_int, _i32p,
@@ -63,14 +65,18 @@ def _bits(x) -> np.ndarray:
     return x
 
 
-def quantize_keys(k: np.ndarray):
-    """k: [n, d] fp16 -> (codes [n, d] uint8, scale [n, d/32] fp16, zero [n, d/32] fp16)."""
+def quantize_keys(k: np.ndarray, bits: int = 4):
+    """k: [n, d] fp16 -> (codes [n, d] uint8, scale [n, d/32] fp16, zero [n, d/32] fp16);
+    bits 4 (the estimate's key cache) or 2 (the variant the pages ablate)."""
     k = _bits(k)
     n, d = k.shape
     codes = np.zeros((n, d), np.uint8)
     scale = np.zeros((n, d // 32), np.uint16)
     zero = np.zeros((n, d // 32), np.uint16)
-    rc = lib().orc_quantize_keys(k, n, d, codes, scale, zero)
+    if bits == 4:
+        rc = lib().orc_quantize_keys(k, n, d, codes, scale, zero)
+    else:
+        rc = lib().orc_quantize_keys_bits(k, n, d, int(bits), codes, scale, zero)
     if rc != 0:
         raise ValueError("orc_quantize_keys failed")
     return codes, scale.view(np.float16), zero.view(np.float16)
@@ -179,7 +185,7 @@ def nearest_half_of_ratio(num: float, den: int) -> int:
 
 
 def run_unit(q_group, k, v, budget, p, sm_scale, page_size: int = 16,
-             headwise: bool = False):
+             headwise: bool = False, key_bits: int = 4):
     """Whole hot path for one (sequence, KV head) unit, stage by stage.
 
     q_group: [G, d] fp16 (the query heads sharing the KV head); k, v: [n, d] fp16 logical
@@ -192,9 +198,11 @@ def run_unit(q_group, k, v, budget, p, sm_scale, page_size: int = 16,
     orc_topp_select with G = 1 on that head's own weights, over the same Quest candidates,
     and its output is attention over its own kept set; kept is then a list of G arrays and
     tau a list of G floats.
+
+    key_bits: 4, or 2 for the estimate from the 2-bit key cache (the pages' ablation).
     """
     n = k.shape[0]
-    codes, scale, zero = quantize_keys(k)
+    codes, scale, zero = quantize_keys(k, key_bits)
     res = {"codes": codes, "scale": scale, "zero": zero}
     P = -(-n // page_size)
     if budget is None:

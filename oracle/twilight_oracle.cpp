@@ -108,17 +108,20 @@ extern "C" {
 // Oracle ABI version, bumped when a function's contract changes.
 int orc_version() { return 1; }
 
-// ---- c1: int4 key quantizer -----------------------------------------------------------
-// Per token and per group of 32 consecutive channels: zero = min, scale = the binary16
-// value nearest (ties to even) to (max - min)/15, code_c = the c in 0..15 whose
-// dequantized value zero + c*scale is nearest to x_c (ties to the even code), and every
-// code is 0 when scale is 0. Nearest-code is the same as clamp(round((x-zero)/scale))
-// with half-to-even rounding, written as a brute-force search over the 16 codes.
+// ---- c1: key quantizer (4-bit, and the 2-bit variant the pages ablate) ------------------
+// Per token and per group of 32 consecutive channels, with L = 2^bits - 1 levels above
+// zero: zero = min, scale = the binary16 value nearest (ties to even) to (max - min)/L,
+// code_c = the c in 0..L whose dequantized value zero + c*scale is nearest to x_c (ties to
+// the even code), and every code is 0 when scale is 0. Nearest-code is the same as
+// clamp(round((x-zero)/scale), 0, L) with half-to-even rounding, written as a brute-force
+// search over the L + 1 codes. The 2-bit form (atlas.scime.ai ablation table: 4-bit is
+// preferred over 2-bit for the estimate's stability) keeps the same group of 32 channels.
 // k: [n_tokens, d] binary16; codes: [n_tokens, d] one code per byte;
 // scale, zero: [n_tokens, d/32] binary16. Returns 0, or -1 on bad input.
-int orc_quantize_keys(const uint16_t* k, int64_t n_tokens, int d, uint8_t* codes,
-                      uint16_t* scale, uint16_t* zero) {
-  if (d <= 0 || d % 32 != 0 || n_tokens < 0) return -1;
+int orc_quantize_keys_bits(const uint16_t* k, int64_t n_tokens, int d, int bits,
+                           uint8_t* codes, uint16_t* scale, uint16_t* zero) {
+  if (d <= 0 || d % 32 != 0 || n_tokens < 0 || (bits != 2 && bits != 4)) return -1;
+  const int levels = (1 << bits) - 1;
   const int ng = d / 32;
   for (int64_t t = 0; t < n_tokens; ++t) {
     for (int g = 0; g < ng; ++g) {
@@ -132,7 +135,7 @@ int orc_quantize_keys(const uint16_t* k, int64_t n_tokens, int d, uint8_t* codes
         if (v > mx) mx = v;
       }
       // -0.0 and +0.0 are both the minimum value 0; store the bit pattern that occurred.
-      const uint16_t s_bits = nearest_h_of_ratio(mx - mn, 15);
+      const uint16_t s_bits = nearest_h_of_ratio(mx - mn, levels);
       const double s = h2d(s_bits);
       scale[t * ng + g] = s_bits;
       zero[t * ng + g] = mn_bits;
@@ -141,7 +144,7 @@ int orc_quantize_keys(const uint16_t* k, int64_t n_tokens, int d, uint8_t* codes
         if (s > 0.0) {
           const double xv = h2d(x[c]);
           double best_err = -1.0;
-          for (int code = 0; code < 16; ++code) {
+          for (int code = 0; code <= levels; ++code) {
             const double err = std::fabs((xv - mn) - code * s);  // exact
             if (best_err < 0.0 || err < best_err ||
                 (err == best_err && (code % 2 == 0) && (best % 2 == 1))) {
@@ -155,6 +158,12 @@ int orc_quantize_keys(const uint16_t* k, int64_t n_tokens, int d, uint8_t* codes
     }
   }
   return 0;
+}
+
+// The 4-bit quantizer of the estimate (atlas.scime.ai "Approach": a 4-bit key cache).
+int orc_quantize_keys(const uint16_t* k, int64_t n_tokens, int d, uint8_t* codes,
+                      uint16_t* scale, uint16_t* zero) {
+  return orc_quantize_keys_bits(k, n_tokens, d, 4, codes, scale, zero);
 }
 
 // ---- c2: Quest per-page channelwise key bounds ----------------------------------------

@@ -55,38 +55,63 @@ def test_nearest_half_of_ratio_matches_numpy_rounding():
 
 # --------------------------------------------------------------------- c1 quantizer ----
 
-def _numpy_quantizer(k):
+def _numpy_quantizer(k, bits=4):
     """Independent formulation: divide and round half-to-even in fp64, then clamp."""
+    L = 2 ** bits - 1
     n, d = k.shape
     x = k.astype(np.float64).reshape(n, d // 32, 32)
     mn = x.min(-1)
     mx = x.max(-1)
-    scale = ((mx - mn) / 15.0).astype(np.float16)
+    scale = ((mx - mn) / L).astype(np.float16)
     s64 = scale.astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        codes = np.where(s64 > 0, np.clip(np.rint((x - mn[..., None]) / s64), 0, 15), 0)
+        codes = np.where(s64 > 0, np.clip(np.rint((x - mn[..., None]) / s64), 0, L), 0)
     return codes.reshape(n, d).astype(np.uint8), scale, mn.astype(np.float16)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("d", [64, 128])
-def test_quantizer_matches_independent_division_rounding(d):
+def test_quantizer_matches_independent_division_rounding(d, bits):
     k = RNG.standard_normal((300, d)).astype(np.float16)
-    codes, scale, zero = oracle.quantize_keys(k)
-    c2, s2, z2 = _numpy_quantizer(k)
+    codes, scale, zero = oracle.quantize_keys(k, bits)
+    c2, s2, z2 = _numpy_quantizer(k, bits)
     assert np.array_equal(codes, c2)
     assert np.array_equal(scale.astype(np.float64), s2.astype(np.float64))
     assert np.array_equal(zero.astype(np.float64), z2.astype(np.float64))
 
 
-def test_quantizer_nearest_code_over_all_16():
+@pytest.mark.parametrize("bits", [4, 2])
+def test_quantizer_nearest_code_over_all_levels(bits):
     k = (RNG.standard_normal((64, 64)) * 2).astype(np.float16)
-    codes, scale, zero = oracle.quantize_keys(k)
+    codes, scale, zero = oracle.quantize_keys(k, bits)
+    assert codes.max() <= 2 ** bits - 1
     x = k.astype(np.float64)
     s = np.repeat(scale.astype(np.float64), 32, axis=1)
     z = np.repeat(zero.astype(np.float64), 32, axis=1)
     err_chosen = np.abs(x - (z + codes * s))
-    for c in range(16):
+    for c in range(2 ** bits):
         assert np.all(err_chosen <= np.abs(x - (z + c * s)))
+
+
+def test_two_bit_quantizer_fixed_points():
+    # scale = (max - min)/3 and four levels; ties between levels go to the even code
+    s_unit = 2.0 ** -2
+    k = np.zeros((2, 32), np.float16)
+    k[0, :] = -0.5                                 # constant: scale 0, codes 0, zero -0.5
+    k[1, 1] = 3 * s_unit                           # max -> scale = s_unit exactly
+    k[1, 2] = 0.5 * s_unit                         # tie 0/1 -> 0
+    k[1, 3] = 1.5 * s_unit                         # tie 1/2 -> 2
+    k[1, 4] = 2.5 * s_unit                         # tie 2/3 -> 2
+    k[1, 5] = 1.25 * s_unit                        # nearest 1
+    codes, scale, zero = oracle.quantize_keys(k, 2)
+    assert scale[0, 0] == 0 and zero[0, 0] == np.float16(-0.5) and np.all(codes[0] == 0)
+    assert float(scale[1, 0]) == s_unit and float(zero[1, 0]) == 0.0
+    assert list(codes[1, :6]) == [0, 3, 0, 2, 2, 1]
+    # (max - min)/3 is not a binary16 value: the scale is its nearest one
+    k2 = np.zeros((1, 32), np.float16)
+    k2[0, 7] = 1.0
+    _, s2, _ = oracle.quantize_keys(k2, 2)
+    assert s2[0, 0] == np.float16(1.0 / 3.0)
 
 
 def test_quantizer_lossless_grid_recovers_codes():
