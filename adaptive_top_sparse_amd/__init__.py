@@ -43,7 +43,7 @@ class Layout(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("num_phys_pages", ctypes.c_int32), ("page_table", ctypes.c_void_p),
-                ("seq_lens", ctypes.c_void_p)]
+                ("seq_lens", ctypes.c_void_p), ("key_bits", ctypes.c_int32)]
 
 
 _lib = None
@@ -114,7 +114,7 @@ def _check(fn: str, status: int):
 
 
 def make_layout(page_table, seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                num_phys_pages: int) -> Layout:
+                num_phys_pages: int, key_bits: int = 4) -> Layout:
     """twl_layout_t for int32 GPU tensors page_table [B, max_pages] and seq_lens [B].
 
     The tensors must outlive every call made with the layout."""
@@ -124,7 +124,7 @@ def make_layout(page_table, seq_lens, num_q_heads: int, num_kv_heads: int, head_
                   head_dim=head_dim, page_size=PAGE_SIZE, max_pages_per_seq=max_pages,
                   num_phys_pages=num_phys_pages,
                   page_table=_ptr(page_table, torch.int32, "page_table"),
-                  seq_lens=_ptr(seq_lens, torch.int32, "seq_lens"))
+                  seq_lens=_ptr(seq_lens, torch.int32, "seq_lens"), key_bits=key_bits)
 
 
 # ---- the C ABI, one function each -------------------------------------------------------

@@ -9,23 +9,22 @@
 namespace twl {
 namespace {
 
-// One lane per (token, 32-channel group). A wave covers one (page, KV head) block of
-// 16 tokens x d channels when d = 128 (64 lanes = 16 tokens x 4 groups), so its loads are
-// one contiguous 4 KiB stretch.
-//
+// Codes of one 32-channel group, BITS (4, or 2 for the ablated variant) per channel:
 // zero = min (the first occurrence of the minimum's bit pattern), scale = the fp16 nearest
-// to (max - min) / 15 (fp64 quotient, one RNE rounding to fp16), and
-// code = clamp(rint((x - zero) / scale), 0, 15) in fp64. fp64 decides every code exactly:
+// to (max - min) / Lv with Lv = 2^BITS - 1 (fp64 quotient, one RNE rounding to fp16), and
+// code = clamp(rint((x - zero) / scale), 0, Lv) in fp64. fp64 decides every code exactly:
 // (x - zero) and scale are multiples of 2^-24 below 2^17, so a quotient that is not a
 // half-integer lies at least 2^-41 away from one, far beyond the fp64 quotient's error;
 // half-integers are exact and rint sends them to the even code.
-// Quantizes the 32-channel group g of token `slot` of physical page `phys` (KV head kvh).
-template <int D>
+// Quantizes the group g of token `slot` of physical page `phys` (KV head kvh).
+template <int D, int BITS>
 __device__ __forceinline__ void quantize_group(const uint16_t* __restrict__ k_cache, int Hkv,
                                                int phys, int kvh, int slot, int g,
                                                uint8_t* __restrict__ codes,
                                                uint32_t* __restrict__ meta) {
   constexpr int NG = D / 32;
+  constexpr int kLevels = (1 << BITS) - 1;
+  constexpr int kWords = BITS;  // 32 codes of BITS bits
   const long row = (static_cast<long>(phys) * Hkv + kvh) * kPage + slot;
   const u32x4* src = reinterpret_cast<const u32x4*>(k_cache + row * D + g * 32);
   uint16_t x[32];
@@ -50,33 +49,33 @@ __device__ __forceinline__ void quantize_group(const uint16_t* __restrict__ k_ca
     mx = fmaxf(mx, v);
   }
   const double zero = static_cast<double>(mn);
-  const uint16_t s_bits = f64_to_f16_bits_nonneg((static_cast<double>(mx) - zero) / 15.0);
+  const uint16_t s_bits =
+      f64_to_f16_bits_nonneg((static_cast<double>(mx) - zero) / static_cast<double>(kLevels));
   const double s = static_cast<double>(h2f(s_bits));
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  uint32_t packed[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) packed[i] = 0u;
   if (s > 0.0) {
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
       double code = rint((static_cast<double>(h2f(x[c])) - zero) / s);
-      code = code > 15.0 ? 15.0 : code;
-      packed[c / 8] |= static_cast<uint32_t>(code) << (4 * (c % 8));
+      code = code > kLevels ? kLevels : code;
+      packed[c * BITS / 32] |= static_cast<uint32_t>(code) << (BITS * c % 32);
     }
   }
-  u32x4 out = {packed[0], packed[1], packed[2], packed[3]};
-  *reinterpret_cast<u32x4*>(codes + row * (D / 2) + g * 16) = out;
+  uint8_t* dst = codes + row * (D * BITS / 8) + g * (4 * BITS);
+  if constexpr (BITS == 4) {
+    *reinterpret_cast<u32x4*>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  } else {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+  }
   meta[row * NG + g] = static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(mn_bits) << 16);
 }
 
 // Whole-cache (prefill) form: one lane per (token, 32-channel group). A wave covers one
 // (page, KV head) block of 16 tokens x d channels when d = 128 (64 lanes = 16 tokens x 4
 // groups), so its loads are one contiguous 4 KiB stretch.
-//
-// zero = min (the first occurrence of the minimum's bit pattern), scale = the fp16 nearest
-// to (max - min) / 15 (fp64 quotient, one RNE rounding to fp16), and
-// code = clamp(rint((x - zero) / scale), 0, 15) in fp64. fp64 decides every code exactly:
-// (x - zero) and scale are multiples of 2^-24 below 2^17, so a quotient that is not a
-// half-integer lies at least 2^-41 away from one, far beyond the fp64 quotient's error;
-// half-integers are exact and rint sends them to the even code.
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(256) void quantize_keys_kernel(
     const uint16_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, int Hkv, int max_pages, int num_phys,
@@ -94,7 +93,7 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(
   if (tok >= n) return;
   const int phys = page_table[static_cast<long>(b) * max_pages + page];
   if (!phys_ok(phys, num_phys)) return;
-  quantize_group<D>(k_cache, Hkv, phys, kvh, slot, g, codes, meta);
+  quantize_group<D, BITS>(k_cache, Hkv, phys, kvh, slot, g, codes, meta);
 }
 
 // The 16 rows of one (physical page, KV head) block, D / 64 channels per lane (lane l owns
@@ -163,17 +162,20 @@ __device__ __forceinline__ uint32_t f16_order_key(uint16_t bits) {
   return (bits & 0x8000u) && mag != 0 ? 0x7fffu - mag : 0x8000u + mag;
 }
 
-// Int4 codes of one token row held across the wave (the same rule as quantize_group, so
-// both forms write identical bytes): the lanes of each 32-channel group find the group's
-// first minimum (smallest key, then smallest channel) and its maximum together, then each
-// lane codes its own channels. `row` is the row index [phys, kvh, slot].
-template <int D>
+// Codes of one token row held across the wave (the same rule as quantize_group, so both
+// forms write identical bytes): the lanes of each 32-channel group find the group's first
+// minimum (smallest key, then smallest channel) and its maximum together, then each lane
+// codes its own channels and the lanes sharing a byte combine theirs. `row` is the row
+// index [phys, kvh, slot].
+template <int D, int BITS>
 __device__ __forceinline__ void quantize_row_wave(const uint16_t (&x)[D / 64], long row,
                                                   uint8_t* __restrict__ codes,
                                                   uint32_t* __restrict__ meta) {
   constexpr int CPL = D / 64;
-  constexpr int LPG = 32 / CPL;  // lanes per 32-channel group
+  constexpr int LPG = 32 / CPL;              // lanes per 32-channel group
+  constexpr int LPB = 8 / (CPL * BITS);      // lanes per code byte
   constexpr int NG = D / 32;
+  constexpr int kLevels = (1 << BITS) - 1;
   const int lane = lane_id();
   float v[CPL];
 #pragma unroll
@@ -204,25 +206,25 @@ __device__ __forceinline__ void quantize_row_wave(const uint16_t (&x)[D / 64], l
       __shfl(static_cast<int>(both), (lane / LPG) * LPG + ch / CPL));
   const uint16_t mn_bits = static_cast<uint16_t>(CPL > 1 && (ch & 1) ? w >> 16 : w & 0xffffu);
   const double zero = static_cast<double>(h2f(mn_bits));
-  const uint16_t s_bits = f64_to_f16_bits_nonneg((static_cast<double>(mx) - zero) / 15.0);
+  const uint16_t s_bits =
+      f64_to_f16_bits_nonneg((static_cast<double>(mx) - zero) / static_cast<double>(kLevels));
   const double s = static_cast<double>(h2f(s_bits));
-  uint32_t code[CPL];
+  uint32_t bits = 0;  // this lane's CPL codes, lowest channel in the lowest bits
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     double q = 0.0;
     if (s > 0.0) {
       q = rint((static_cast<double>(v[c]) - zero) / s);
-      q = q > 15.0 ? 15.0 : q;
+      q = q > kLevels ? kLevels : q;
     }
-    code[c] = static_cast<uint32_t>(q);
+    bits |= static_cast<uint32_t>(q) << (BITS * c);
   }
-  uint8_t* dst = codes + row * (D / 2);
-  if constexpr (CPL == 2) {
-    dst[lane] = static_cast<uint8_t>(code[0] | (code[1] << 4));
-  } else {
-    const uint32_t odd = static_cast<uint32_t>(__shfl_xor(static_cast<int>(code[0]), 1));
-    if ((lane & 1) == 0) dst[lane / 2] = static_cast<uint8_t>(code[0] | (odd << 4));
-  }
+  uint32_t byte = bits;
+#pragma unroll
+  for (int i = 1; i < LPB; ++i)
+    byte |= static_cast<uint32_t>(__shfl(static_cast<int>(bits), (lane & ~(LPB - 1)) + i))
+            << (i * CPL * BITS);
+  if (lane % LPB == 0) codes[row * (D * BITS / 8) + lane / LPB] = static_cast<uint8_t>(byte);
   if (lane % LPG == 0)
     meta[row * NG + lane / LPG] = static_cast<uint32_t>(s_bits) | (static_cast<uint32_t>(mn_bits) << 16);
 }
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256) void page_bounds_kernel(
 // tokens at or after token_begin[b] (one page for a one-token append). Each page's rows are
 // loaded once and serve both its bounds (kBounds) and the codes of its tokens at or after
 // token_begin (kCodes), so a decode step's cache maintenance is a single short launch.
-template <int D, bool kCodes, bool kBounds>
+template <int D, int BITS, bool kCodes, bool kBounds>
 __global__ __launch_bounds__(kWave) void append_keys_kernel(
     const uint16_t* __restrict__ k_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ token_begin, int Hkv,
@@ -283,22 +285,46 @@ __global__ __launch_bounds__(kWave) void append_keys_kernel(
 #pragma unroll
           for (int t = 1; t < kPage; ++t) x[c] = slot == t ? r.x[t][c] : x[c];
         }
-        quantize_row_wave<D>(x, row0 + slot, codes, meta);
+        quantize_row_wave<D, BITS>(x, row0 + slot, codes, meta);
       }
     }
+  }
+}
+
+template <int D, bool kCodes, bool kBounds>
+void launch_append_d(const Layout& L, const uint16_t* k, const int32_t* token_begin,
+                     uint8_t* codes, uint32_t* meta, uint16_t* mm, hipStream_t s) {
+  const dim3 grid(L.Hkv, L.B);
+  if (L.bits == 2) {
+    append_keys_kernel<D, 2, kCodes, kBounds><<<grid, kWave, 0, s>>>(
+        k, L.page_table, L.seq_lens, token_begin, L.Hkv, L.max_pages, L.num_phys, codes, meta, mm);
+  } else {
+    append_keys_kernel<D, 4, kCodes, kBounds><<<grid, kWave, 0, s>>>(
+        k, L.page_table, L.seq_lens, token_begin, L.Hkv, L.max_pages, L.num_phys, codes, meta, mm);
   }
 }
 
 template <bool kCodes, bool kBounds>
 void launch_append(const Layout& L, const uint16_t* k, const int32_t* token_begin,
                    uint8_t* codes, uint32_t* meta, uint16_t* mm, hipStream_t s) {
-  const dim3 grid(L.Hkv, L.B);
   if (L.d == 128) {
-    append_keys_kernel<128, kCodes, kBounds><<<grid, kWave, 0, s>>>(
-        k, L.page_table, L.seq_lens, token_begin, L.Hkv, L.max_pages, L.num_phys, codes, meta, mm);
+    launch_append_d<128, kCodes, kBounds>(L, k, token_begin, codes, meta, mm, s);
   } else {
-    append_keys_kernel<64, kCodes, kBounds><<<grid, kWave, 0, s>>>(
-        k, L.page_table, L.seq_lens, token_begin, L.Hkv, L.max_pages, L.num_phys, codes, meta, mm);
+    launch_append_d<64, kCodes, kBounds>(L, k, token_begin, codes, meta, mm, s);
+  }
+}
+
+template <int D>
+void launch_quantize_d(const Layout& L, const uint16_t* k, uint8_t* codes, uint32_t* m,
+                       hipStream_t s) {
+  const long items = static_cast<long>(L.max_pages) * L.Hkv * kPage * (D / 32);
+  const dim3 grid(static_cast<unsigned>((items + 255) / 256), L.B);
+  if (L.bits == 2) {
+    quantize_keys_kernel<D, 2><<<grid, 256, 0, s>>>(k, L.page_table, L.seq_lens, L.Hkv,
+                                                    L.max_pages, L.num_phys, codes, m);
+  } else {
+    quantize_keys_kernel<D, 4><<<grid, 256, 0, s>>>(k, L.page_table, L.seq_lens, L.Hkv,
+                                                    L.max_pages, L.num_phys, codes, m);
   }
 }
 
@@ -312,14 +338,10 @@ hipError_t launch_quantize_keys(const Layout& L, const void* k_cache, const int3
     launch_append<true, false>(L, k, token_begin, codes, m, nullptr, s);
     return hipGetLastError();
   }
-  const long items = static_cast<long>(L.max_pages) * L.Hkv * kPage * (L.d / 32);
-  const dim3 grid(static_cast<unsigned>((items + 255) / 256), L.B);
   if (L.d == 128) {
-    quantize_keys_kernel<128><<<grid, 256, 0, s>>>(k, L.page_table, L.seq_lens, L.Hkv,
-                                                    L.max_pages, L.num_phys, codes, m);
+    launch_quantize_d<128>(L, k, codes, m, s);
   } else {
-    quantize_keys_kernel<64><<<grid, 256, 0, s>>>(k, L.page_table, L.seq_lens, L.Hkv,
-                                                   L.max_pages, L.num_phys, codes, m);
+    launch_quantize_d<64>(L, k, codes, m, s);
   }
   return hipGetLastError();
 }

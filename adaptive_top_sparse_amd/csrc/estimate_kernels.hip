@@ -1,7 +1,8 @@
 // Twilight's attention-weight estimate over the candidate tokens from the int4 key cache
 // (Twilight pages, atlas.scime.ai summary "Approach": top-p runs on estimated weights of
 // the pre-selected tokens, computed from a 4-bit quantized key cache; "Limitations": the
-// estimate's own cost matters when token loading is not the bottleneck).
+// estimate's own cost matters when token loading is not the bottleneck). The 2-bit key
+// cache of the pages' ablation runs through the same kernel with BITS = 2.
 //
 // Per candidate token j and query head h of the group:
 //   s_hj = sm_scale * sum_groups [zero * Q_grp,h + scale * sum_{c in grp} q_hc * code_c],
@@ -32,7 +33,7 @@ constexpr int kNormSlots = kNormThreads * 16;  // weights per normalization work
 // The dot products run on the matrix cores, one 16-token tile (a candidate page) at a time,
 // with v_mfma_f32_16x16x16_f16 (lane l supplies A[l%16][4(l/16)..+3] and
 // B[4(l/16)..+3][l%16] and receives D[4(l/16)..+3][l%16]):
-//  * B = channels x tokens: the 4-bit codes as exact fp16 integers. Lane group c4 = l/16
+//  * B = channels x tokens: the codes as exact fp16 integers. Lane group c4 = l/16
 //    supplies "virtual group" c4, the c4-th quarter of the channels (D/4 of them, one
 //    contiguous run of the token's code row), four channels per instruction.
 //  * A = rows (c4, h) = virtual group x query head, block-diagonal: row (c4, h) carries
@@ -43,15 +44,25 @@ constexpr int kNormSlots = kNormThreads * 16;  // weights per normalization work
 // Lane (t, c4) scales its group's dot products (scale, plus zero * Q_grp once per real
 // group), the four lane groups' terms are summed across rows, and lane (t, c4) keeps head
 // c4 (and c4 + 4). A dot product is invariant to a common permutation of both operands, so
-// the channel slots are ordered for cheap unpacking ({0,4,1,5} then {2,6,3,7} within each
-// 8-channel word); every product of an fp16 q and a code is exact in fp32.
+// the channel slots are ordered for cheap unpacking: a mask of the same few bits of both
+// 16-bit halves of a code word yields two codes at once. With 4-bit codes a word holds 8
+// channels and instruction pair (2w, 2w+1) takes its slots {0,4,1,5} and {2,6,3,7}; with
+// 2-bit codes a word holds 16 channels and instructions 4w..4w+3 take {0,8,1,9}, {2,10,3,11},
+// {4,12,5,13}, {6,14,7,15}. Every product of an fp16 q and a code is exact in fp32.
+template <int BITS>
 __device__ __forceinline__ int mfma_channel(int c4, int vg_channels, int m, int e) {
-  constexpr int kPerm[2][4] = {{0, 4, 1, 5}, {2, 6, 3, 7}};
-  return c4 * vg_channels + 8 * (m / 2) + kPerm[m % 2][e];
+  if constexpr (BITS == 4) {
+    constexpr int kPerm[2][4] = {{0, 4, 1, 5}, {2, 6, 3, 7}};
+    return c4 * vg_channels + 8 * (m / 2) + kPerm[m % 2][e];
+  } else {
+    const int mm = m % 4;
+    return c4 * vg_channels + 16 * (m / 4) + 2 * mm + (e % 2) * 8 + e / 2;
+  }
 }
 
-// Two fp16 codes from the nibble pair at bits [3:0] and [19:16]: 1024 + n is exact in fp16
-// (its ulp is 1), so or-ing n into the significand of 1024 and subtracting 1024 gives n.
+// Two fp16 codes from the bit fields at [3:0] and [19:16] (of which only the low BITS are
+// set): 1024 + n is exact in fp16 (its ulp is 1), so or-ing n into the significand of 1024
+// and subtracting 1024 gives n.
 __device__ __forceinline__ uint32_t codes_to_f16x2(uint32_t pair_bits) {
   const f16x2 v = __builtin_bit_cast(f16x2, pair_bits | 0x64006400u);
   const f16x2 r = v - f16x2{static_cast<f16>(1024.f), static_cast<f16>(1024.f)};
@@ -71,6 +82,8 @@ __device__ __forceinline__ CodeWords<NG> load_words(const uint32_t* p) {
     r.w[1] = v[1];
     r.w[2] = v[2];
     r.w[3] = v[3];
+  } else if constexpr (NG == 1) {
+    r.w[0] = *p;
   } else {
     const u32x2 v = *reinterpret_cast<const u32x2*>(p);
     r.w[0] = v[0];
@@ -84,7 +97,7 @@ __device__ __forceinline__ CodeWords<NG> load_words(const uint32_t* p) {
 // MFMA tile per page. Each page goes through three dependent loads (candidate page id, page
 // table, codes and metadata), pipelined across batches: ids two batches ahead, page-table
 // entries and codes one ahead. The chunk's (max, sum exp) per head is kept online per lane.
-template <int D, int G>
+template <int D, int G, int BITS>
 __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint32_t* __restrict__ meta, const int32_t* __restrict__ page_table,
@@ -97,6 +110,8 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   constexpr int MPT = D / 16;         // instructions per tile and head set
   constexpr int NHB = (G + 3) / 4;    // head sets of up to 4 heads
   constexpr int PB = kEstBatch;
+  constexpr int NW = VG * BITS / 32;  // code words per lane and token
+  constexpr int RB = D * BITS / 8;    // code bytes per token row
   static_assert(G <= 8, "at most 8 query heads per KV head");
   __shared__ f16 qs[G][D];
   __shared__ float qsum[G][NG];
@@ -147,20 +162,19 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     }
   };
   // this lane's codes (virtual group c4 of its token's row) and its group's {scale, zero}
-  auto load_codes = [&](int (&pid)[PB], const int (&phys)[PB], CodeWords<VG / 8> (&cw)[PB],
+  auto load_codes = [&](int (&pid)[PB], const int (&phys)[PB], CodeWords<NW> (&cw)[PB],
                         uint32_t (&mw)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const bool ok = pid[i] >= 0 && phys_ok(phys[i], num_phys);
       pid[i] = ok ? pid[i] : -1;
       const long row = ok ? (static_cast<long>(phys[i]) * Hkv + g) * kPage + tok_in_page : 0;
-      cw[i] = load_words<VG / 8>(reinterpret_cast<const uint32_t*>(codes + row * (D / 2)) +
-                                 c4 * (VG / 8));
+      cw[i] = load_words<NW>(reinterpret_cast<const uint32_t*>(codes + row * RB) + c4 * NW);
       mw[i] = meta[row * NG + c4 * VG / 32];
     }
   };
   int phys0[PB], phys1[PB];
-  CodeWords<VG / 8> cw0[PB];
+  CodeWords<NW> cw0[PB];
   uint32_t mw0[PB];
   load_phys(0, ids0, phys0);
   load_codes(ids0, phys0, cw0, mw0);
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       for (int m = 0; m < MPT; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          qa[hb][m][e] = (vg == c4 && h < G) ? qs[h < G ? h : 0][mfma_channel(c4, VG, m, e)]
+          qa[hb][m][e] = (vg == c4 && h < G) ? qs[h < G ? h : 0][mfma_channel<BITS>(c4, VG, m, e)]
                                              : static_cast<f16>(0.f);
     }
   }
@@ -216,23 +230,26 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   for (int j = 0; j < n_batches; ++j) {
     int ids2[PB];
     if (j + 2 < n_batches) load_ids(j + 2, ids2);
-    CodeWords<VG / 8> cw1[PB];
+    CodeWords<NW> cw1[PB];
     uint32_t mw1[PB];
     if (j + 1 < n_batches) load_codes(ids1, phys1, cw1, mw1);
 
     float s[PB][NHB];
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      // B operands of the tile: two instructions per 32-bit word of codes
+      // B operands of the tile: 32 / (4 BITS) instructions per 32-bit word of codes
       f16x4 bq[MPT];
 #pragma unroll
-      for (int wi = 0; wi < VG / 8; ++wi) {
+      for (int wi = 0; wi < NW; ++wi) {
         const uint32_t w = cw0[i].w[wi];
-        uint32_t bw[4];
+        constexpr int kPairs = 16 / BITS;  // code pairs per word
+        constexpr uint32_t kMask = BITS == 4 ? 0x000f000fu : 0x00030003u;
+        uint32_t bw[kPairs];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) bw[k] = codes_to_f16x2((w >> (4 * k)) & 0x000f000fu);
-        bq[2 * wi] = __builtin_bit_cast(f16x4, u32x2{bw[0], bw[1]});
-        bq[2 * wi + 1] = __builtin_bit_cast(f16x4, u32x2{bw[2], bw[3]});
+        for (int k = 0; k < kPairs; ++k) bw[k] = codes_to_f16x2((w >> (BITS * k)) & kMask);
+#pragma unroll
+        for (int m = 0; m < kPairs / 2; ++m)
+          bq[wi * (kPairs / 2) + m] = __builtin_bit_cast(f16x4, u32x2{bw[2 * m], bw[2 * m + 1]});
       }
       const float scale = h2f(static_cast<uint16_t>(mw0[i] & 0xffffu));
       const float zero = h2f(static_cast<uint16_t>(mw0[i] >> 16));
@@ -379,27 +396,42 @@ __global__ __launch_bounds__(kNormThreads) void estimate_normalize_kernel(
   }
 }
 
-template <int D, int G>
+template <int D, int G, int BITS>
 void logits_launch(const Layout& L, const void* q, const uint8_t* codes, const void* meta,
                    const int32_t* cand_pages, const int32_t* cand_count, int stride,
                    float sm_scale, float* weights, float2* partials, int chunk_pages,
                    int n_chunks, hipStream_t s) {
-  estimate_logits_kernel<D, G><<<dim3(n_chunks, L.Hkv, L.B), kEstChunk, 0, s>>>(
+  estimate_logits_kernel<D, G, BITS><<<dim3(n_chunks, L.Hkv, L.B), kEstChunk, 0, s>>>(
       static_cast<const uint16_t*>(q), codes, static_cast<const uint32_t*>(meta), L.page_table,
       L.seq_lens, cand_pages, cand_count, stride, L.Hkv, L.max_pages, L.num_phys, sm_scale,
       weights, partials, chunk_pages, n_chunks);
 }
 
-template <int D>
+template <int D, int BITS>
 void logits_dispatch_g(const Layout& L, const void* q, const uint8_t* codes, const void* meta,
                        const int32_t* cand_pages, const int32_t* cand_count, int stride,
                        float sm_scale, float* weights, float2* partials, int chunk_pages,
                        int n_chunks, hipStream_t s) {
   switch (L.G()) {
-    case 1: logits_launch<D, 1>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
-    case 2: logits_launch<D, 2>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
-    case 4: logits_launch<D, 4>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
-    default: logits_launch<D, 8>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+    case 1: logits_launch<D, 1, BITS>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+    case 2: logits_launch<D, 2, BITS>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+    case 4: logits_launch<D, 4, BITS>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+    default: logits_launch<D, 8, BITS>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale, weights, partials, chunk_pages, n_chunks, s); break;
+  }
+}
+
+template <int D>
+void logits_dispatch_bits(const Layout& L, const void* q, const uint8_t* codes,
+                          const void* meta, const int32_t* cand_pages,
+                          const int32_t* cand_count, int stride, float sm_scale,
+                          float* weights, float2* partials, int chunk_pages, int n_chunks,
+                          hipStream_t s) {
+  if (L.bits == 2) {
+    logits_dispatch_g<D, 2>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale,
+                            weights, partials, chunk_pages, n_chunks, s);
+  } else {
+    logits_dispatch_g<D, 4>(L, q, codes, meta, cand_pages, cand_count, stride, sm_scale,
+                            weights, partials, chunk_pages, n_chunks, s);
   }
 }
 
@@ -430,11 +462,11 @@ hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes,
   const int n_chunks = (cand_stride_pages + cp - 1) / cp;
   float2* partials = static_cast<float2*>(stage_scratch(ws, L));
   if (L.d == 128) {
-    logits_dispatch_g<128>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
-                           sm_scale, weights, partials, cp, n_chunks, s);
+    logits_dispatch_bits<128>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
+                              sm_scale, weights, partials, cp, n_chunks, s);
   } else {
-    logits_dispatch_g<64>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
-                          sm_scale, weights, partials, cp, n_chunks, s);
+    logits_dispatch_bits<64>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
+                             sm_scale, weights, partials, cp, n_chunks, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

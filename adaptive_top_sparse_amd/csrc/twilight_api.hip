@@ -39,8 +39,10 @@ int check_layout(const twl_layout_t* L, Layout* out, bool* empty) {
              !aligned4(L->seq_lens)) {
     return TWL_ERR_INVALID_ARG;
   }
+  if (L->key_bits != 0 && L->key_bits != 4 && L->key_bits != 2) return TWL_ERR_UNSUPPORTED;
   *out = Layout{L->batch,     L->num_q_heads,     L->num_kv_heads,  L->head_dim,
                 L->max_pages_per_seq, L->num_phys_pages, L->page_table, L->seq_lens};
+  out->bits = L->key_bits == 2 ? 2 : 4;
   return TWL_OK;
 }
 

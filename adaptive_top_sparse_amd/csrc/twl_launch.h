@@ -17,6 +17,7 @@ struct Layout {
   int B, Hq, Hkv, d, max_pages, num_phys;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  int bits = 4;  // width of the estimate's key codes: 4 or 2
   // Top-p and decode units: one kept set per KV head, shared by its G query heads
   // (group-wise), or one per query head (head-wise).
   bool headwise = false;

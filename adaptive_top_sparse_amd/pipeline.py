@@ -43,10 +43,11 @@ class DeviceCache:
     k_meta: torch.Tensor
     page_minmax: Optional[torch.Tensor]
     last_token: torch.Tensor  # seq_len - 1 (>= 0) per sequence: the newest token
+    key_bits: int = 4         # width of the estimate's key codes (4, or 2)
 
     def layout(self):
         return make_layout(self.page_table, self.seq_lens, self.Hq, self.Hkv, self.d,
-                           self.num_phys)
+                           self.num_phys, self.key_bits)
 
     @property
     def max_pages(self) -> int:
@@ -79,7 +80,8 @@ class DeviceCache:
         return DeviceCache(**rep)
 
 
-def upload(w, device="cuda", with_bounds: Optional[bool] = None) -> DeviceCache:
+def upload(w, device="cuda", with_bounds: Optional[bool] = None,
+           key_bits: int = 4) -> DeviceCache:
     """Copy a workloads.Workload to the GPU (caches in the paged layout) and allocate the
     int4 key cache and the page bounds it needs."""
     s = w.spec
@@ -96,11 +98,13 @@ def upload(w, device="cuda", with_bounds: Optional[bool] = None) -> DeviceCache:
         seq_lens=torch.from_numpy(w.seq_lens).to(dev),
         q=torch.from_numpy(w.q).to(dev),
         k_cache=k_paged, v_cache=v_paged,
-        k_codes=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 2), dtype=torch.uint8, device=dev),
+        k_codes=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d * key_bits // 8), dtype=torch.uint8,
+                            device=dev),
         k_meta=torch.zeros((P, s.Hkv, PAGE_SIZE, s.d // 32, 2), dtype=torch.float16, device=dev),
         page_minmax=(torch.zeros((s.B, s.Hkv, w.max_pages, 2, s.d), dtype=torch.float16,
                                  device=dev) if with_bounds else None),
-        last_token=torch.from_numpy(np.maximum(w.seq_lens.astype(np.int32) - 1, 0)).to(dev))
+        last_token=torch.from_numpy(np.maximum(w.seq_lens.astype(np.int32) - 1, 0)).to(dev),
+        key_bits=key_bits)
 
 
 @dataclasses.dataclass

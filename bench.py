@@ -250,6 +250,90 @@ def time_headwise(reps, bufs, p, stream, steps, warmup):
             "kept_token_heads_groupwise": int(bufs[0].kept_count.sum().item()) * G}
 
 
+def _replay_us(graphs, stream, steps, warmup):
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def time_two_bit(w, p, stream, steps, warmup, replicas, buf4):
+    """The 2-bit key cache the pages ablate (4-bit keeps the estimated weights more stable):
+    the step on its own layer replicas (hipGraph replays in rotation), and the stability of
+    both widths' kept sets on the first replica, measured against the exact weights
+    (softmax of q.k on the fp16 keys over the same candidates, fp64, group mean): the exact
+    mass each kept set captures (p is the target) and the overlap of the two sets."""
+    import torch
+    from adaptive_top_sparse_amd import pipeline
+    s = w.spec
+    base = pipeline.upload(w, key_bits=2)
+    base.build_caches()
+    torch.cuda.synchronize()
+    # replicas while they fit beside the 4-bit ones (two already defeat the 256 MB
+    # Infinity Cache when a layer's caches are larger than it)
+    rep_bytes = sum(t.numel() * t.element_size() for t in vars(base).values()
+                    if isinstance(t, torch.Tensor))
+    fit = int(torch.cuda.mem_get_info()[0] * 0.6 // max(1, rep_bytes))
+    replicas = max(2, min(replicas, fit + 1))
+    reps = [base] + [base.clone() for _ in range(replicas - 1)]
+    bufs = [pipeline.alloc_step(r) for r in reps]
+    graphs = []
+    for c, b in zip(reps, bufs):
+        with torch.cuda.stream(stream):
+            pipeline.run_step(c, b, p, stream=stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            pipeline.run_step(c, b, p, stream=stream)
+        graphs.append(g)
+    us = _replay_us(graphs, stream, steps, warmup)
+    k2, c2 = bufs[0].kept.cpu().numpy(), bufs[0].kept_count.cpu().numpy()
+    k4, c4 = buf4.kept.cpu().numpy(), buf4.kept_count.cpu().numpy()
+    sel = None if buf4.sel_pages is None else buf4.sel_pages.cpu().numpy()
+    sel_n = None if buf4.sel_count is None else buf4.sel_count.cpu().numpy()
+    del graphs, bufs, reps, base
+    torch.cuda.empty_cache()
+    G = s.G
+    sm = pipeline.default_sm_scale(s.d)
+    m2, m4, jac = [], [], []
+    for b in range(s.B):
+        n = int(w.seq_lens[b])
+        if n == 0:
+            continue
+        for g in range(s.Hkv):
+            if sel is None:
+                toks = np.arange(n)
+            else:
+                pages = sel[b, g, :sel_n[b, g]].astype(np.int64)
+                toks = (pages[:, None] * 16 + np.arange(16)).reshape(-1)
+                toks = toks[toks < n]
+            q = w.q[b, g * G:(g + 1) * G].astype(np.float64)
+            lg = float(sm) * (q @ w.k[b][g][toks].astype(np.float64).T)
+            e = np.exp(lg - lg.max(1, keepdims=True))
+            Wx = (e / e.sum(1, keepdims=True)).mean(0)
+            a = k2[b, g, :c2[b, g]]
+            c = k4[b, g, :c4[b, g]]
+            m2.append(float(Wx[np.searchsorted(toks, a)].sum()))
+            m4.append(float(Wx[np.searchsorted(toks, c)].sum()))
+            jac.append(len(np.intersect1d(a, c)) / max(1, len(np.union1d(a, c))))
+    return {"step_us": us, "layer_replicas": replicas,
+            "estimate_bytes_per_token": s.d // 4 + (s.d // 32) * 4,
+            "kept_2bit": int(c2.sum()), "kept_4bit": int(c4.sum()),
+            "exact_mass_kept_2bit": float(np.mean(m2)), "exact_mass_kept_4bit": float(np.mean(m4)),
+            "exact_mass_kept_2bit_min": float(np.min(m2)),
+            "exact_mass_kept_4bit_min": float(np.min(m4)),
+            "kept_set_jaccard_2bit_vs_4bit": float(np.mean(jac))}
+
+
 def cpu_baseline(w, p, seconds):
     """The fp64 oracle (stages select, estimate, top-p, attention; the cache is quantized
     beforehand, as on the GPU) on whole decode steps of the same workload, single thread,
@@ -426,6 +510,7 @@ def main():
         "baselines": None,
         "decode_loop": None,
         "headwise": None,
+        "key_bits_2": None,
         "cpu_baseline": None,
     }
     if not args.no_baselines:
@@ -439,6 +524,9 @@ def main():
         if reps[0].Hq != reps[0].Hkv:
             print("[bench] timing the head-wise step", file=sys.stderr, flush=True)
             res["headwise"] = time_headwise(reps, bufs, p, stream, args.steps, args.warmup)
+        print("[bench] timing the 2-bit key cache variant", file=sys.stderr, flush=True)
+        res["key_bits_2"] = time_two_bit(w, p, stream, args.steps, args.warmup, len(reps),
+                                         bufs[0])
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, p, args.cpu_seconds)

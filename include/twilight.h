@@ -39,8 +39,9 @@
  *   page_minmax      : fp16  [B, Hkv, max_pages_per_seq, 2, d] in LOGICAL page order of
  *                      each sequence, row 0 = min, row 1 = max (so one KV head's bounds are
  *                      one contiguous stretch that the page scorer streams)
- *   k_codes          : uint8 [num_phys_pages, Hkv, 16, d/2] byte i = channel 2i in the
- *                      low nibble, channel 2i+1 in the high nibble
+ *   k_codes          : uint8 [num_phys_pages, Hkv, 16, d * key_bits / 8]; 4-bit: byte i
+ *                      = channel 2i in the low nibble, channel 2i+1 in the high nibble;
+ *                      2-bit: byte i = channels 4i .. 4i+3 from the low bits up
  *   k_meta           : fp16  [num_phys_pages, Hkv, 16, d/32, 2] {scale, zero} per group
  *   page_table       : int32 [B, max_pages_per_seq] logical page -> physical page
  *   seq_lens         : int32 [B]
@@ -75,14 +76,18 @@ typedef struct twl_layout {
   int32_t num_phys_pages;    /* leading extent of the paged caches, >= 1 */
   const int32_t* page_table; /* device [B, max_pages_per_seq] */
   const int32_t* seq_lens;   /* device [B] */
+  int32_t key_bits;          /* width of the estimate's key codes: 4 (0 also means 4), or
+                                2, the variant the pages ablate (atlas.scime.ai ablation
+                                table: 4-bit keeps the estimated weights more stable) */
 } twl_layout_t;
 
 /* Int4 key cache for the weight estimate (atlas.scime.ai "Approach": weights are
  * estimated from a 4-bit quantized key cache; "Limitations": it costs about 1/8 of the
  * KV cache, which is what the codes take at 4 of fp16 K+V's 32 bits per channel).
- * Per token, KV head and group of 32 channels: zero = min, scale = the fp16 value nearest
- * (ties to even) to (max - min) / 15, code = the c in 0..15 whose zero + c*scale is nearest
- * to x (ties to the even code); every code is 0 when scale is 0. Quantizes tokens
+ * Per token, KV head and group of 32 channels, with Lv = 2^key_bits - 1 (15, or 3 for
+ * 2-bit codes): zero = min, scale = the fp16 value nearest (ties to even) to
+ * (max - min) / Lv, code = the c in 0..Lv whose zero + c*scale is nearest to x (ties to
+ * the even code); every code is 0 when scale is 0. Quantizes tokens
  * [token_begin[b], seq_len_b) of each sequence (token_begin NULL means 0), so a decode
  * step can append one token. Writes k_codes and k_meta at those tokens only. */
 int twilight_quantize_keys(const twl_layout_t* L, const void* k_cache,

@@ -36,14 +36,15 @@ def logical_rows(paged: np.ndarray, page_table_row: np.ndarray, n: int, kvh: int
     return blk.reshape((P * PAGE,) + blk.shape[2:])[:n]
 
 
-def unpack_codes(packed: np.ndarray) -> np.ndarray:
-    """[n, d/2] bytes -> [n, d] codes; channel 2i is the low nibble of byte i."""
-    lo = packed & 0x0F
-    hi = packed >> 4
-    return np.stack([lo, hi], axis=-1).reshape(packed.shape[0], -1)
+def unpack_codes(packed: np.ndarray, bits: int = 4) -> np.ndarray:
+    """[n, d * bits / 8] bytes -> [n, d] codes; a byte holds 8 / bits channels, the lowest
+    channel in the lowest bits."""
+    per = 8 // bits
+    fields = [(packed >> (bits * i)) & ((1 << bits) - 1) for i in range(per)]
+    return np.stack(fields, axis=-1).reshape(packed.shape[0], -1)
 
 
-def oracle_units(w, p: float, units=None, headwise: bool = False):
+def oracle_units(w, p: float, units=None, headwise: bool = False, key_bits: int = 4):
     """Oracle results per (b, kvh) unit (all units, or the listed ones)."""
     s = w.spec
     G = s.G
@@ -53,7 +54,7 @@ def oracle_units(w, p: float, units=None, headwise: bool = False):
     res = {}
     for b, g in units:
         res[(b, g)] = oracle.run_unit(w.q[b, g * G:(g + 1) * G], w.k[b][g], w.v[b][g],
-                                      w.budget, p, sm, headwise=headwise)
+                                      w.budget, p, sm, headwise=headwise, key_bits=key_bits)
     return res
 
 

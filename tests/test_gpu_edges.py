@@ -321,13 +321,14 @@ def _crafted_group(kind: int, rng) -> np.ndarray:
     return f16(x)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("d", [128, 64])
-def test_append_keys_tie_rules_match_oracle(d):
+def test_append_keys_tie_rules_match_oracle(d, bits):
     pl = _pipeline()
-    print(f"\n[edge] append quantizer tie rules, d={d}", flush=True)
+    print(f"\n[edge] append quantizer tie rules, d={d}, {bits}-bit", flush=True)
     w = workloads.make_workload(4, B=2, seq_lens=[77, 260], budget=8, Hq=4, Hkv=4, d=d)
     rng = np.random.default_rng(11)
-    c = pl.upload(w)
+    c = pl.upload(w, key_bits=bits)
     kh = c.k_cache.cpu().numpy().view(np.uint16).copy()           # [P, Hkv, 16, d]
     back = 40
     for b in range(2):
@@ -355,10 +356,10 @@ def test_append_keys_tie_rules_match_oracle(d):
         pt = w.page_table[b]
         for kvh in range(4):
             rows = parity.logical_rows(kh, pt, n, kvh)[n - back:]
-            o_codes, o_scale, o_zero = oracle.quantize_keys(rows.view(np.float16))
+            o_codes, o_scale, o_zero = oracle.quantize_keys(rows.view(np.float16), bits)
             got_codes = parity.logical_rows(codes_h, pt, n, kvh)[n - back:]
             got_meta = parity.logical_rows(meta_h, pt, n, kvh)[n - back:]
-            assert np.array_equal(parity.unpack_codes(got_codes), o_codes), (b, kvh)
+            assert np.array_equal(parity.unpack_codes(got_codes, bits), o_codes), (b, kvh)
             assert np.array_equal(got_meta[..., 0], o_scale.view(np.uint16)), (b, kvh)
             assert np.array_equal(got_meta[..., 1], o_zero.view(np.uint16)), (b, kvh)
             assert np.array_equal(got_codes, parity.logical_rows(full[0], pt, n, kvh)[n - back:])

@@ -28,12 +28,18 @@ CASES = {
     # units above 32768 slots keep half of W in LDS: GQA (wide pass) and MHA (direct)
     "cfg5-n40k": (5, dict(B=1, n=40000 + 3), 0.9),
     "cfg5-n40k-mha": (5, dict(B=1, n=40000 + 3, Hq=4, Hkv=4), 0.9),
+    # the 2-bit key cache of the pages' ablation: every head dim, group size and selector
+    "cfg1-2bit": (1, {}, 0.9, 2),
+    "cfg3s-2bit": (3, dict(n=8192 + 5, budget=64), 0.9, 2),
+    "cfg3s-2bit-g8": (3, dict(n=3000 + 1, budget=32, Hq=16, Hkv=2), 0.85, 2),
+    "cfg4s-2bit": (4, dict(B=4, n_range=(40, 3000), budget=32), 0.85, 2),
+    "cfg5s-2bit-g2-d64": (5, dict(B=2, n=4096 + 11, Hq=8, Hkv=4, d=64), 0.9, 2),
 }
 
 
-def _run(w, p, repeat=1):
+def _run(w, p, repeat=1, key_bits=4):
     from adaptive_top_sparse_amd import pipeline
-    c = pipeline.upload(w)
+    c = pipeline.upload(w, key_bits=key_bits)
     c.build_caches()
     buf = pipeline.alloc_step(c)
     outs = []
@@ -52,12 +58,14 @@ def _run(w, p, repeat=1):
 
 @pytest.fixture(scope="module", params=list(CASES))
 def case(request):
-    cfg, over, p = CASES[request.param]
-    print(f"\n[parity case] {request.param} cfg={cfg} {over} p={p}", flush=True)
+    cfg, over, p, *rest = CASES[request.param]
+    bits = rest[0] if rest else 4
+    print(f"\n[parity case] {request.param} cfg={cfg} {over} p={p} key_bits={bits}", flush=True)
     w = workloads.make_workload(cfg, **over)
-    c, host, outs = _run(w, p, repeat=2)
-    orc = parity.oracle_units(w, p)
-    return dict(name=request.param, w=w, p=p, host=host, out=outs[0], out2=outs[1], orc=orc)
+    c, host, outs = _run(w, p, repeat=2, key_bits=bits)
+    orc = parity.oracle_units(w, p, key_bits=bits)
+    return dict(name=request.param, w=w, p=p, host=host, out=outs[0], out2=outs[1], orc=orc,
+                bits=bits)
 
 
 def test_quantized_keys_bit_exact(case):
@@ -66,7 +74,8 @@ def test_quantized_keys_bit_exact(case):
         n = int(w.seq_lens[b])
         if n == 0:
             continue
-        codes = parity.unpack_codes(parity.logical_rows(host["k_codes"], w.page_table[b], n, g))
+        codes = parity.unpack_codes(parity.logical_rows(host["k_codes"], w.page_table[b], n, g),
+                                    case["bits"])
         assert np.array_equal(codes, res["codes"]), (b, g)
         meta = parity.logical_rows(host["k_meta"], w.page_table[b], n, g)
         assert np.array_equal(meta[..., 0].astype(np.float64), res["scale"].astype(np.float64))
