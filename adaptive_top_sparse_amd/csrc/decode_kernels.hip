@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   constexpr int BSTEP = decode_batch_tokens(D);
   __shared__ float s_m[kDecWaves][G], s_l[kDecWaves][G];
   __shared__ float s_acc[kDecWaves][G][D];
+  TWL_PHASE_BEGIN(0, 32);
   TWL_PHASE(0);
   TWL_SPAN_BEGIN();
 
@@ -330,6 +331,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     }
   }
   TWL_PHASE(3);
+  TWL_PHASE_FLUSH(0, 32);
   TWL_SPAN_END();
 }
 

@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   __shared__ f16 qs[G][D];
   __shared__ float qsum[G][NG];
   __shared__ float red_m[kEstWaves][G], red_l[kEstWaves][G];
+  TWL_PHASE_BEGIN(0, 32);
   TWL_PHASE(0);
   const int b = blockIdx.z;
   const int g = blockIdx.y;
@@ -349,6 +350,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(M, L);
   }
   TWL_PHASE(3);
+  TWL_PHASE_FLUSH(0, 32);
 }
 
 // w = exp(s - M) / L with (M, L) merged from the row's chunk partials; invalid slots hold

@@ -101,6 +101,7 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
   constexpr int ROUNDS = kScoreRounds;
   constexpr int PPB = PPI * ROUNDS;
   static_assert(ROUNDS == 4, "the round reduction handles four rounds");
+  TWL_PHASE_BEGIN(0, 4);
   TWL_PHASE(0);
   TWL_SPAN_BEGIN();
   const int b = blockIdx.z;
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
   if (writes_round<LPP>() && p < P)
     scores[(static_cast<long>(b) * Hkv + g) * score_row_stride(max_pages) + p] = total;
   TWL_PHASE(2);
+  TWL_PHASE_FLUSH(0, 4);
   TWL_SPAN_END();
 }
 
@@ -206,6 +208,7 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   __shared__ uint32_t n_short;
   __shared__ uint64_t short_key[kWave + 1];
   __shared__ int short_page[kWave + 1];
+  TWL_PHASE_BEGIN(4, 32);
   TWL_PHASE(4);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   if (threadIdx.x == 0) sel_count[unit] = m;
   if (m == P) {
     for (int i = threadIdx.x; i < P; i += NT) out[i] = i;
+    TWL_PHASE_FLUSH(4, 32);
     return;
   }
   const double* sc = scores + unit * score_row_stride(max_pages);
@@ -396,6 +400,7 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   for (int i = 0; i < KPT; ++i)
     if (chosen[i]) out[pos++] = first + i;
   TWL_PHASE(13);
+  TWL_PHASE_FLUSH(4, 32);
 }
 
 template <int NT, int KPT>

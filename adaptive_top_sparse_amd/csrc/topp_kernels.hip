@@ -185,6 +185,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   __shared__ uint64_t red64[NW];
   __shared__ uint64_t pick[3];
   __shared__ uint32_t n_short[2], short_keys[kWave + 1];
+  TWL_PHASE_BEGIN(0, 32);
   TWL_PHASE(0);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
@@ -418,6 +419,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     if (tau_out) tau_out[unit] = tau;
   }
   TWL_PHASE(11);
+  TWL_PHASE_FLUSH(0, 32);
 }
 
 // Everything a launch needs besides the kernel's template arguments.

@@ -6,21 +6,44 @@
 
 #include "twl_launch.h"
 
-// Opt-in phase timing for tuning builds (-DTWL_PHASE_TIMING): work-group 0 / thread 0 of a
-// kernel stores the 100 MHz real-time clock at marked phase boundaries (and the shader clock
-// counter at entry 32 + i) in a per-file device array that
-// an exported twl_phase_<file>() copies out. Compiled out otherwise.
+// Opt-in phase timing for tuning builds (-DTWL_PHASE_TIMING): thread 0 of work-group 0 of a
+// kernel stamps the 100 MHz real-time clock (and the shader clock at entry 32 + i) at
+// marked phase boundaries into LDS, and TWL_PHASE_FLUSH at the kernel's end copies the
+// stamps to a per-file device array that an exported twl_phase_<file>() copies out. The
+// stamps stay in LDS until the end because a global store before a block barrier would
+// make that barrier wait for the store to complete. Compiled out otherwise.
 #ifdef TWL_PHASE_TIMING
+__device__ __forceinline__ unsigned long long* twl_phase_lds() {
+  __shared__ unsigned long long ts[64];
+  return ts;
+}
 #define TWL_PHASE_STORAGE(NAME)                                                       \
   static __device__ unsigned long long twl_phase_ts[64];                              \
   extern "C" void twl_phase_##NAME(unsigned long long* host) {                        \
     (void)hipMemcpyFromSymbol(host, HIP_SYMBOL(twl_phase_ts), sizeof(twl_phase_ts));  \
   }
+// TWL_PHASE_BEGIN(lo, hi) at kernel entry clears the kernel's own stamp range [lo, hi)
+// (kernels of one file own disjoint ranges), TWL_PHASE_FLUSH(lo, hi) copies it out.
+#define TWL_PHASE_BEGIN(lo, hi)                                                        \
+  do {                                                                                 \
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {   \
+      for (int z_ = (lo); z_ < (hi); ++z_) twl_phase_lds()[z_] = twl_phase_lds()[32 + z_] = 0ull; \
+    }                                                                                  \
+  } while (0)
 #define TWL_PHASE(i)                                                                   \
   do {                                                                                 \
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {   \
-      twl_phase_ts[i] = __builtin_amdgcn_s_memrealtime();                              \
-      twl_phase_ts[32 + (i)] = __builtin_amdgcn_s_memtime();                           \
+      twl_phase_lds()[i] = __builtin_amdgcn_s_memrealtime();                           \
+      twl_phase_lds()[32 + (i)] = __builtin_amdgcn_s_memtime();                        \
+    }                                                                                  \
+  } while (0)
+#define TWL_PHASE_FLUSH(lo, hi)                                                        \
+  do {                                                                                 \
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {   \
+      for (int z_ = (lo); z_ < (hi); ++z_) {                                           \
+        twl_phase_ts[z_] = twl_phase_lds()[z_];                                        \
+        twl_phase_ts[32 + z_] = twl_phase_lds()[32 + z_];                              \
+      }                                                                                \
     }                                                                                  \
   } while (0)
 // start and end clock of every work-group (linear id < 32768) and the XCC it ran on
@@ -52,8 +75,14 @@
   do {                 \
   } while (0)
 #define TWL_PHASE_STORAGE(NAME)
+#define TWL_PHASE_BEGIN(lo, hi) \
+  do {                          \
+  } while (0)
 #define TWL_PHASE(i) \
   do {               \
+  } while (0)
+#define TWL_PHASE_FLUSH(lo, hi) \
+  do {                          \
   } while (0)
 #endif
 
