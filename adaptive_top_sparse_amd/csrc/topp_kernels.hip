@@ -57,15 +57,17 @@ struct ToppShape {
 };
 
 // floor(W * 2^(40 - e)) for a non-negative fp32 W given by its bits, e the binary exponent
-// of the unit's largest W: integer shifts of the 24-bit significand (W < 2^(e+1), so the
-// result is below 2^41). Subnormal W (a tiny share of any sum) counts as 0.
+// of the unit's largest W (W < 2^(e+1), so the result is below 2^41). Subnormal W (a tiny
+// share of any sum) counts as 0. x = W * 2^(40-e) is exact in fp32 (a power-of-two
+// scaling); its integer part above 2^32 converts exactly, and x minus that part is again
+// exact in fp32 (it keeps at most x's 24 significant bits), so two truncating conversions
+// give floor(x) with no 64-bit shifts.
 __device__ __forceinline__ uint64_t fixed_mass(uint32_t key, int e) {
-  const int ew = static_cast<int>(key >> 23) - 127;
-  if (ew < -126) return 0;
-  const uint64_t sig = (key & 0x7fffffu) | 0x800000u;
-  const int sh = ew - e + 17;  // W * 2^(40-e) = sig * 2^(ew - 23 + 40 - e)
-  if (sh >= 0) return sig << sh;
-  return sh <= -24 ? 0 : (sig >> (-sh));
+  if ((key >> 23) == 0) return 0;
+  const float x = ldexpf(__uint_as_float(key), 40 - e);
+  const uint32_t hi = static_cast<uint32_t>(x * 0x1p-32f);
+  const uint32_t lo = static_cast<uint32_t>(fmaf(-static_cast<float>(hi), 0x1p32f, x));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 template <int VW>
@@ -102,6 +104,9 @@ __device__ __forceinline__ int page_token(const int32_t* cand_row, int cnt, int 
   if (s0 / kPage >= cnt || pid < 0 || pid >= max_pages) return -1;
   return pid * kPage + s0 % kPage;
 }
+
+// Marks a vector whose first token is not known yet (tokens are >= -1).
+constexpr int kNoToken = -2;
 
 // Candidate pages in the row of unit `unit` (0 without a page list).
 __device__ __forceinline__ int candidate_pages(const int32_t* cand_pages,
@@ -207,8 +212,12 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   // multiple of 16, so a vector that starts inside the row ends inside it, and vectors past
   // the row load slot 0 instead, so that no load sits behind a branch.
   float W[NR][VW];
+  // token of each register vector's first slot (-1: not a candidate), kept while it costs
+  // few registers; wider shapes look the tokens up again when compacting
+  constexpr bool kKeepT0 = SPT <= 16;
+  int T0[NR];
   uint32_t kmax = 0, kmin = 0xffffffffu;
-  auto form_batch = [&](auto nb_tag, int v0, float (*dst)[VW]) {
+  auto form_batch = [&](auto nb_tag, int v0, float (*dst)[VW], int* t0_out) {
     constexpr int NB = decltype(nb_tag)::value;
     float x[NB][G][VW];
     int pid[NB];
@@ -225,6 +234,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     for (int i = 0; i < NB; ++i) {
       const int s0 = wbase + (v0 + i) * kWave * VW + lane * VW;
       const int t0 = s0 < n_slots ? page_token(cand_row, cnt, max_pages, s0, pid[i]) : -1;
+      if (t0_out != nullptr) t0_out[i] = t0;
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
         float acc = 0.f;
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
 #pragma unroll 1
     for (int v = 0; v < NL; v += kBatch) {
       float w[kBatch][VW];
-      form_batch(std::integral_constant<int, kBatch>(), NR + v, w);
+      form_batch(std::integral_constant<int, kBatch>(), NR + v, w, nullptr);
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
         w_lds[(v + i) * NT + threadIdx.x] =
@@ -257,7 +267,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   constexpr int kRegBatch = NR < S::kRegBatch ? NR : S::kRegBatch;
 #pragma unroll
   for (int v = 0; v < NR; v += kRegBatch)
-    form_batch(std::integral_constant<int, kRegBatch>(), v, W + v);
+    form_batch(std::integral_constant<int, kRegBatch>(), v, W + v, kKeepT0 ? T0 + v : nullptr);
   TWL_PHASE(1);
   block_minmax<NT, uint32_t>(kmin, kmax, red_a, red_b, 0xffffffffu, 0u, &kmin, &kmax);
   TWL_PHASE(2);
@@ -399,21 +409,36 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   }
   TWL_PHASE(10);
   int32_t* out = kept + unit * n_slots;
-  for_each_w([&](int v, const float(&w)[VW]) {
+  // register vectors reuse the tokens found while forming W; LDS vectors look them up
+  auto emit = [&](int v, const float(&w)[VW], int t0_known) {
     uint32_t c = 0;
 #pragma unroll
     for (int j = 0; j < VW; ++j) c += (w[j] > 0.f && w[j] >= tau) ? 1u : 0u;
     const uint32_t incl = wave_incl_scan(c);
     if (c != 0) {
       const int s0 = wbase + v * kWave * VW + lane * VW;
-      const int t0 = page_token(cand_row, cnt, max_pages, s0, page_id_of(cand_row, cnt, s0));
+      const int t0 = t0_known != kNoToken
+                         ? t0_known
+                         : page_token(cand_row, cnt, max_pages, s0, page_id_of(cand_row, cnt, s0));
       uint32_t pos = run + incl - c;
 #pragma unroll
       for (int j = 0; j < VW; ++j)
         if (w[j] > 0.f && w[j] >= tau) out[pos++] = t0 + j;
     }
     run += readlane(incl, kWave - 1);
-  });
+  };
+#pragma unroll
+  for (int v = 0; v < NR; ++v) emit(v, W[v], kKeepT0 ? T0[v] : kNoToken);
+  if constexpr (NL > 0) {
+#pragma unroll 2
+    for (int v = 0; v < NL; ++v) {
+      const f32x4 t = w_lds[v * NT + threadIdx.x];
+      float w[VW];
+#pragma unroll
+      for (int j = 0; j < VW; ++j) w[j] = t[j];
+      emit(NR + v, w, kNoToken);
+    }
+  }
   if (threadIdx.x == 0) {
     kept_count[unit] = static_cast<int32_t>(total);
     if (tau_out) tau_out[unit] = tau;
