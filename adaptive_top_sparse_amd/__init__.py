@@ -27,7 +27,8 @@ TWL_ERR_LAUNCH = -4
 EXPORTED = ("twilight_quantize_keys", "quest_page_bounds", "quest_select_pages",
             "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode",
             "twilight_append_keys", "twilight_topp_select_headwise",
-            "twilight_sparse_decode_headwise", "twilight_workspace_size",
+            "twilight_sparse_decode_headwise", "twilight_estimate_topp",
+            "twilight_estimate_topp_headwise", "twilight_workspace_size",
             "twilight_status_string")
 
 
@@ -68,7 +69,9 @@ def lib():
         L.twilight_append_keys.argtypes = [LP, P, P, P, P, P, P]
         L.twilight_topp_select_headwise.argtypes = L.twilight_topp_select.argtypes
         L.twilight_sparse_decode_headwise.argtypes = L.twilight_sparse_decode.argtypes
-        for name in EXPORTED[:9]:
+        L.twilight_estimate_topp.argtypes = [LP, P, P, P, P, P, I32, F, F, P, P, P, P, P, SZ, P]
+        L.twilight_estimate_topp_headwise.argtypes = L.twilight_estimate_topp.argtypes
+        for name in EXPORTED[:11]:
             getattr(L, name).restype = ctypes.c_int
         L.twilight_workspace_size.argtypes = [LP, I32]
         L.twilight_workspace_size.restype = ctypes.c_size_t
@@ -202,6 +205,40 @@ def _topp_select(name: str, layout: Layout, weights, cand_pages, cand_count,
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(name, st)
+
+
+def _estimate_topp(name: str, layout: Layout, q, k_codes, k_meta, cand_pages, cand_count,
+                   cand_stride_pages: int, sm_scale: float, p: float, weights, kept,
+                   kept_count, tau, workspace, stream=None) -> None:
+    import torch
+    st = getattr(lib(), name)(
+        ctypes.byref(layout), _ptr(q, torch.float16, "q"), _ptr(k_codes, torch.uint8, "k_codes"),
+        _ptr(k_meta, torch.float16, "k_meta"), _ptr(cand_pages, torch.int32, "cand_pages"),
+        _ptr(cand_count, torch.int32, "cand_count"), int(cand_stride_pages), float(sm_scale),
+        float(p), _ptr(weights, torch.float32, "weights"), _ptr(kept, torch.int32, "kept"),
+        _ptr(kept_count, torch.int32, "kept_count"), _ptr(tau, torch.float32, "tau"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(name, st)
+
+
+def twilight_estimate_topp(layout: Layout, q, k_codes, k_meta, cand_pages, cand_count,
+                           cand_stride_pages: int, sm_scale: float, p: float, weights, kept,
+                           kept_count, tau, workspace, stream=None) -> None:
+    """Estimate and group-wise top-p in one call (weights is scratch)."""
+    _estimate_topp("twilight_estimate_topp", layout, q, k_codes, k_meta, cand_pages,
+                   cand_count, cand_stride_pages, sm_scale, p, weights, kept, kept_count, tau,
+                   workspace, stream)
+
+
+def twilight_estimate_topp_headwise(layout: Layout, q, k_codes, k_meta, cand_pages,
+                                    cand_count, cand_stride_pages: int, sm_scale: float,
+                                    p: float, weights, kept, kept_count, tau, workspace,
+                                    stream=None) -> None:
+    """Estimate and head-wise top-p in one call (weights is scratch)."""
+    _estimate_topp("twilight_estimate_topp_headwise", layout, q, k_codes, k_meta, cand_pages,
+                   cand_count, cand_stride_pages, sm_scale, p, weights, kept, kept_count, tau,
+                   workspace, stream)
 
 
 def twilight_topp_select(layout: Layout, weights, cand_pages, cand_count,

@@ -8,7 +8,8 @@
 //   s_hj = sm_scale * sum_groups [zero * Q_grp,h + scale * sum_{c in grp} q_hc * code_c],
 // with Q_grp,h = sum_{c in grp} q_hc, the same value as q_h . dequant(k_j). Then a softmax
 // over the unit's valid candidates, done as per-chunk (max, sum of exp) partials followed
-// by a normalization pass.
+// by a normalization pass. The logits are kept in log2 units (s_hj * log2 e), so that every
+// exponential is one exp2.
 #include "twl_device.h"
 #include "twl_launch.h"
 
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     const uint32_t* __restrict__ meta, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages, int Hkv, int max_pages,
-    int num_phys, float sm_scale, float* __restrict__ logits, float2* __restrict__ partials,
+    int num_phys, float scale_log2, float* __restrict__ logits, float2* __restrict__ partials,
     int chunk_pages, int n_chunks) {
   constexpr int NG = D / 32;
   constexpr int VG = D / 4;           // channels per virtual group (lane group)
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
         }
         // lane group c4 keeps head c4 + 4 hb
         const float mine = c4 == 0 ? tot[0] : c4 == 1 ? tot[1] : c4 == 2 ? tot[2] : tot[3];
-        s[i][hb] = (valid && c4 + 4 * hb < G) ? sm_scale * mine : -INFINITY;
+        s[i][hb] = (valid && c4 + 4 * hb < G) ? scale_log2 * mine : -INFINITY;
       }
       // logits row entries (every slot of the chunk is written, -inf when not a candidate)
       const int slot = rank_of(j, i) * kPage + tok_in_page;
@@ -302,9 +303,9 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       for (int i = 1; i < PB; ++i) bm = fmaxf(bm, s[i][hb]);
       const float mn = fmaxf(run_m[hb], bm);
       if (mn > -INFINITY) {
-        float l = run_m[hb] > -INFINITY ? run_l[hb] * expf(run_m[hb] - mn) : 0.f;
+        float l = run_m[hb] > -INFINITY ? run_l[hb] * exp2f(run_m[hb] - mn) : 0.f;
 #pragma unroll
-        for (int i = 0; i < PB; ++i) l += s[i][hb] > -INFINITY ? expf(s[i][hb] - mn) : 0.f;
+        for (int i = 0; i < PB; ++i) l += s[i][hb] > -INFINITY ? exp2f(s[i][hb] - mn) : 0.f;
         run_l[hb] = l;
         run_m[hb] = mn;
       }
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const float M = group_reduce<16>(run_m[hb], OpMax());
-    const float l = run_m[hb] > -INFINITY ? run_l[hb] * expf(run_m[hb] - M) : 0.f;
+    const float l = run_m[hb] > -INFINITY ? run_l[hb] * exp2f(run_m[hb] - M) : 0.f;
     const float L = group_reduce<16>(l, OpSum());
     const int h = c4 + 4 * hb;
     if (h < G && tok_in_page == 0) {
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     for (int w2 = 1; w2 < kEstWaves; ++w2) M = fmaxf(M, red_m[w2][h]);
     float L = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kEstWaves; ++w2) L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * expf(red_m[w2][h] - M) : 0.f;
+    for (int w2 = 0; w2 < kEstWaves; ++w2) L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * exp2f(red_m[w2][h] - M) : 0.f;
     partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(M, L);
   }
   TWL_PHASE(3);
@@ -369,31 +370,20 @@ __global__ __launch_bounds__(kNormThreads) void estimate_normalize_kernel(
     v[k] = *reinterpret_cast<const f32x4*>(w + (sl < n_slots ? sl : 0));
   }
   if (threadIdx.x < kWave) {
-    const float2* pr = partials + hrow * n_chunks;
-    float m = -INFINITY, l = 0.f;
-    for (int i = threadIdx.x; i < n_chunks; i += kWave) {
-      const float2 p = pr[i];
-      if (p.x > -INFINITY) {
-        const float mn = fmaxf(m, p.x);
-        l = (m > -INFINITY ? l * expf(m - mn) : 0.f) + p.y * expf(p.x - mn);
-        m = mn;
-      }
-    }
-    const float M = wave_max(m);
-    const float L = wave_sum(m > -INFINITY ? l * expf(m - M) : 0.f);
+    const float2 ml = merge_max_sum_wave(partials + hrow * n_chunks, n_chunks);
     if (threadIdx.x == 0) {
-      s_ml[0] = M;
-      s_ml[1] = L;
+      s_ml[0] = ml.x;
+      s_ml[1] = ml.y;
     }
   }
   __syncthreads();
-  const float M = s_ml[0], L = s_ml[1];
+  const float M = s_ml[0], inv_l = softmax_inv_sum(s_ml[1]);
   if (first >= n_slots) return;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     f32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (L > 0.f && v[k][e] > -INFINITY) ? expf(v[k][e] - M) / L : 0.f;
+    for (int e = 0; e < 4; ++e) o[e] = softmax_weight(v[k][e], M, inv_l);
     *reinterpret_cast<f32x4*>(w + first + 4 * k) = o;
   }
 }
@@ -455,23 +445,29 @@ size_t estimate_workspace_bytes(const Layout& L, int cand_stride_pages) {
   return align_up(static_cast<size_t>(L.B) * L.Hq * n_chunks * sizeof(float2), 256);
 }
 
+int estimate_chunks(const Layout& L, int cand_stride_pages) {
+  const int cp = estimate_chunk_pages(L, cand_stride_pages);
+  return (cand_stride_pages + cp - 1) / cp;
+}
+
 hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes, const void* meta,
                            const int32_t* cand_pages, const int32_t* cand_count,
                            int cand_stride_pages, float sm_scale, float* weights, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, bool normalize) {
   const int n_slots = cand_stride_pages * kPage;
   const int cp = estimate_chunk_pages(L, cand_stride_pages);
-  const int n_chunks = (cand_stride_pages + cp - 1) / cp;
+  const int n_chunks = estimate_chunks(L, cand_stride_pages);
   float2* partials = static_cast<float2*>(stage_scratch(ws, L));
+  const float scale_log2 = sm_scale * 1.4426950408889634f;  // logits in log2 units
   if (L.d == 128) {
     logits_dispatch_bits<128>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
-                              sm_scale, weights, partials, cp, n_chunks, s);
+                              scale_log2, weights, partials, cp, n_chunks, s);
   } else {
     logits_dispatch_bits<64>(L, q, codes, meta, cand_pages, cand_count, cand_stride_pages,
-                             sm_scale, weights, partials, cp, n_chunks, s);
+                             scale_log2, weights, partials, cp, n_chunks, s);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !normalize) return e;
   const dim3 grid((n_slots + kNormSlots - 1) / kNormSlots, L.B * L.Hq);
   estimate_normalize_kernel<<<grid, kNormThreads, 0, s>>>(weights, partials, n_chunks, n_slots);
   return hipGetLastError();

@@ -169,14 +169,18 @@ struct SlotMap {
 };
 
 // `src` holds G rows of n_slots values per unit: the estimate's weights, or (G == 1) the
-// group means formed by topp_mean_kernel, which are already 0 off the candidates.
+// group means formed by topp_mean_kernel, which are already 0 off the candidates. With
+// `norm` given, src holds the estimate's logits instead and norm its per-chunk (max, sum of
+// exp) pairs, norm_chunks per query head; the kernel then normalises each head's logits
+// itself, with the same arithmetic as the estimate's normalising pass, so the weights it
+// sees are bit-identical and that pass (a launch and a round trip of the weights) is saved.
 template <int NT, int G, int SPT>
 __global__ __launch_bounds__(NT) void topp_kernel(
     const float* __restrict__ src, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages,
     const int32_t* __restrict__ seq_lens, int units, int cand_div, int max_pages, float p,
     int32_t* __restrict__ kept, int32_t* __restrict__ kept_count,
-    float* __restrict__ tau_out) {
+    float* __restrict__ tau_out, const float2* __restrict__ norm, int norm_chunks) {
   using M = SlotMap<NT, SPT>;
   using S = ToppShape<NT>;
   constexpr int VW = M::VW, NR = M::NR, NL = M::NL;
@@ -190,6 +194,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   __shared__ uint64_t red64[NW];
   __shared__ uint64_t pick[3];
   __shared__ uint32_t n_short[2], short_keys[kWave + 1];
+  __shared__ float s_norm[2][G];
   TWL_PHASE_BEGIN(0, 32);
   TWL_PHASE(0);
   const int b = blockIdx.y;
@@ -217,10 +222,27 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   constexpr bool kKeepT0 = SPT <= 16;
   int T0[NR];
   uint32_t kmax = 0, kmin = 0xffffffffu;
-  auto form_batch = [&](auto nb_tag, int v0, float (*dst)[VW], int* t0_out) {
-    constexpr int NB = decltype(nb_tag)::value;
-    float x[NB][G][VW];
-    int pid[NB];
+  // each head's max and 1 / (sum of exp2) when normalising here: wave h merges head h's
+  // chunks
+  float nM[G], nL[G];
+  auto norm_stats = [&]() {
+    for (int h = wv; h < G; h += NW) {
+      const float2 ml = merge_max_sum_wave(norm + (unit * G + h) * norm_chunks, norm_chunks);
+      if (lane == 0) {
+        s_norm[0][h] = ml.x;
+        s_norm[1][h] = ml.y;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      nM[h] = s_norm[0][h];
+      nL[h] = softmax_inv_sum(s_norm[1][h]);
+    }
+  };
+  // a batch of NB vectors: all loads (weights and page ids) first, then W
+  auto load_batch = [&](int v0, auto& x, auto& pid) {
+    constexpr int NB = sizeof(pid) / sizeof(pid[0]);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int s0 = wbase + (v0 + i) * kWave * VW + lane * VW;
@@ -230,11 +252,20 @@ __global__ __launch_bounds__(NT) void topp_kernel(
         load_vec<VW>(row0 + static_cast<long>(h) * n_slots + sl, x[i][h]);
       pid[i] = page_id_of(cand_row, cnt, sl);
     }
+  };
+  auto finish_batch = [&](int v0, auto& x, auto& pid, float (*dst)[VW], int* t0_out) {
+    constexpr int NB = sizeof(pid) / sizeof(pid[0]);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int s0 = wbase + (v0 + i) * kWave * VW + lane * VW;
       const int t0 = s0 < n_slots ? page_token(cand_row, cnt, max_pages, s0, pid[i]) : -1;
       if (t0_out != nullptr) t0_out[i] = t0;
+      if (norm != nullptr) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int j = 0; j < VW; ++j) x[i][h][j] = softmax_weight(x[i][h][j], nM[h], nL[h]);
+      }
 #pragma unroll
       for (int j = 0; j < VW; ++j) {
         float acc = 0.f;
@@ -251,23 +282,34 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     }
   };
   if constexpr (NL > 0) {
+    if (norm != nullptr) norm_stats();
     constexpr int kBatch = 4;
     static_assert(NL % kBatch == 0, "LDS vectors come in batches of four");
 #pragma unroll 1
     for (int v = 0; v < NL; v += kBatch) {
+      float x[kBatch][G][VW];
+      int pid[kBatch];
       float w[kBatch][VW];
-      form_batch(std::integral_constant<int, kBatch>(), NR + v, w, nullptr);
+      load_batch(NR + v, x, pid);
+      finish_batch(NR + v, x, pid, w, nullptr);
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
         w_lds[(v + i) * NT + threadIdx.x] =
             f32x4{w[i][0], w[i][1 % VW], w[i][2 % VW], w[i][3 % VW]};
     }
   }
-  // register vectors in batches, which bounds the loads held in flight
+  // register vectors in batches, which bounds the loads held in flight; when normalising
+  // here with no LDS vectors, the first batch's loads go out before the heads' statistics
+  // are merged, so the two latencies overlap
   constexpr int kRegBatch = NR < S::kRegBatch ? NR : S::kRegBatch;
 #pragma unroll
-  for (int v = 0; v < NR; v += kRegBatch)
-    form_batch(std::integral_constant<int, kRegBatch>(), v, W + v, kKeepT0 ? T0 + v : nullptr);
+  for (int v = 0; v < NR; v += kRegBatch) {
+    float x[kRegBatch][G][VW];
+    int pid[kRegBatch];
+    load_batch(v, x, pid);
+    if (NL == 0 && v == 0 && norm != nullptr) norm_stats();
+    finish_batch(v, x, pid, W + v, kKeepT0 ? T0 + v : nullptr);
+  }
   TWL_PHASE(1);
   block_minmax<NT, uint32_t>(kmin, kmax, red_a, red_b, 0xffffffffu, 0u, &kmin, &kmax);
   TWL_PHASE(2);
@@ -460,13 +502,16 @@ struct ToppArgs {
   float* tau;
   float* stage;
   hipStream_t s;
+  const float2* norm;  // non-null: weights hold logits, normalised in the top-p kernel
+  int norm_chunks;
 };
 
 template <int NT, int G, int SPT>
 void launch_main(const ToppArgs& a, const float* src) {
   topp_kernel<NT, G, SPT><<<dim3(a.L->units(), a.L->B), NT, 0, a.s>>>(
       src, a.cand_pages, a.cand_count, a.stride, a.L->seq_lens, a.L->units(),
-      a.L->headwise ? a.L->G() : 1, a.L->max_pages, a.p, a.kept, a.kept_count, a.tau);
+      a.L->headwise ? a.L->G() : 1, a.L->max_pages, a.p, a.kept, a.kept_count, a.tau,
+      src == a.weights ? a.norm : nullptr, a.norm_chunks);
 }
 
 template <int G>
@@ -517,6 +562,10 @@ void launch_spt(const ToppArgs& a) {
 
 }  // namespace
 
+bool topp_can_normalize(const Layout& L, int cand_stride_pages) {
+  return !uses_mean_pass(L.unit_G(), cand_stride_pages * kPage);
+}
+
 size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages) {
   const long n_slots = static_cast<long>(cand_stride_pages) * kPage;
   if (!uses_mean_pass(L.unit_G(), static_cast<int>(n_slots))) return 0;
@@ -526,9 +575,10 @@ size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages) {
 hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* cand_pages,
                        const int32_t* cand_count, int cand_stride_pages, float p,
                        int32_t* kept, int32_t* kept_count, float* tau, void* ws,
-                       hipStream_t s) {
+                       hipStream_t s, const float2* norm, int norm_chunks) {
   const ToppArgs a{&L, weights, cand_pages, cand_count, cand_stride_pages, p, kept,
-                   kept_count, tau, static_cast<float*>(stage_scratch(ws, L)), s};
+                   kept_count, tau, static_cast<float*>(stage_scratch(ws, L)), s, norm,
+                   norm_chunks};
   const int n_slots = cand_stride_pages * kPage;
 #if TWL_TOPP_SMALL_UNIT > 0
   if (block_threads(n_slots) == 256) {

@@ -236,12 +236,77 @@ int twilight_estimate_weights(const twl_layout_t* L, const void* q, const uint8_
                                             stream));
 }
 
+int estimate_topp(bool headwise, const twl_layout_t* L, const void* q, const uint8_t* k_codes,
+                  const void* k_meta, const int32_t* cand_pages, const int32_t* cand_count,
+                  int32_t cand_stride_pages, float sm_scale, float p, float* weights,
+                  int32_t* kept, int32_t* kept_count, float* tau, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  Layout lay{};
+  bool empty = false;
+  int st = check_layout(L, &lay, &empty);
+  if (st != TWL_OK) return st;
+  lay.headwise = headwise;
+  if (q == nullptr || k_codes == nullptr || k_meta == nullptr || weights == nullptr ||
+      kept == nullptr || kept_count == nullptr)
+    return TWL_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned4(k_meta) || !aligned16(weights) ||
+      !aligned4(kept) || !aligned4(kept_count))
+    return TWL_ERR_INVALID_ARG;
+  if (cand_pages != nullptr && !aligned4(cand_pages)) return TWL_ERR_INVALID_ARG;
+  if (cand_count != nullptr && !aligned4(cand_count)) return TWL_ERR_INVALID_ARG;
+  if (tau != nullptr && !aligned4(tau)) return TWL_ERR_INVALID_ARG;
+  if (cand_stride_pages < 1 || !std::isfinite(sm_scale) || !(p > 0.0f && p <= 1.0f))
+    return TWL_ERR_INVALID_ARG;
+  if (cand_pages == nullptr && cand_stride_pages < lay.max_pages) return TWL_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(cand_stride_pages) * twl::kPage > twl::kToppMaxSlots)
+    return TWL_ERR_UNSUPPORTED;
+  if (empty) return TWL_OK;
+  size_t need = twl::estimate_workspace_bytes(lay, cand_stride_pages);
+  const size_t need_t = twl::topp_workspace_bytes(lay, cand_stride_pages);
+  if (need_t > need) need = need_t;
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+    return TWL_ERR_WORKSPACE;
+  // the top-p normalises the logits itself unless a separate group-mean pass is needed
+  const bool fuse = twl::topp_can_normalize(lay, cand_stride_pages);
+  hipError_t e = twl::launch_estimate(lay, q, k_codes, k_meta, cand_pages, cand_count,
+                                      cand_stride_pages, sm_scale, weights, workspace, stream,
+                                      !fuse);
+  if (e != hipSuccess) return TWL_ERR_LAUNCH;
+  return launch_status(twl::launch_topp(
+      lay, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau,
+      workspace, stream, fuse ? static_cast<const float2*>(workspace) : nullptr,
+      fuse ? twl::estimate_chunks(lay, cand_stride_pages) : 0));
+}
+
 int twilight_topp_select(const twl_layout_t* L, const float* weights, const int32_t* cand_pages,
                          const int32_t* cand_count, int32_t cand_stride_pages, float p,
                          int32_t* kept, int32_t* kept_count, float* tau, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
   return topp_select(false, L, weights, cand_pages, cand_count, cand_stride_pages, p, kept,
                      kept_count, tau, workspace, workspace_bytes, stream);
+}
+
+int twilight_estimate_topp(const twl_layout_t* L, const void* q, const uint8_t* k_codes,
+                           const void* k_meta, const int32_t* cand_pages,
+                           const int32_t* cand_count, int32_t cand_stride_pages,
+                           float sm_scale, float p, float* weights, int32_t* kept,
+                           int32_t* kept_count, float* tau, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return estimate_topp(false, L, q, k_codes, k_meta, cand_pages, cand_count, cand_stride_pages,
+                       sm_scale, p, weights, kept, kept_count, tau, workspace, workspace_bytes,
+                       stream);
+}
+
+int twilight_estimate_topp_headwise(const twl_layout_t* L, const void* q,
+                                    const uint8_t* k_codes, const void* k_meta,
+                                    const int32_t* cand_pages, const int32_t* cand_count,
+                                    int32_t cand_stride_pages, float sm_scale, float p,
+                                    float* weights, int32_t* kept, int32_t* kept_count,
+                                    float* tau, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  return estimate_topp(true, L, q, k_codes, k_meta, cand_pages, cand_count, cand_stride_pages,
+                       sm_scale, p, weights, kept, kept_count, tau, workspace, workspace_bytes,
+                       stream);
 }
 
 int twilight_topp_select_headwise(const twl_layout_t* L, const float* weights,

@@ -443,6 +443,37 @@ __device__ __forceinline__ uint32_t block_pick_bucket_lds(const T* bins, T rem, 
   return b;
 }
 
+// ---- softmax normalisation from split partials ----------------------------------------
+
+// Global (max, sum of exp2) of a row of log2-unit logits from its chunks' (max, sum of
+// exp2) pairs, one wave: lane i merges chunks i, i + 64, ... online, then the lanes are
+// combined on the common maximum. Every lane returns the same pair. Chunks with max -inf
+// (no valid slot) are skipped. The estimate's normalising pass and the top-p that
+// normalises for itself both use this, so they agree bit for bit.
+__device__ __forceinline__ float2 merge_max_sum_wave(const float2* pr, int n_chunks) {
+  float m = -INFINITY, l = 0.f;
+  for (int i = lane_id(); i < n_chunks; i += kWave) {
+    const float2 p = pr[i];
+    if (p.x > -INFINITY) {
+      const float mn = fmaxf(m, p.x);
+      l = (m > -INFINITY ? l * exp2f(m - mn) : 0.f) + p.y * exp2f(p.x - mn);
+      m = mn;
+    }
+  }
+  const float M = wave_max(m);
+  const float L = wave_sum(m > -INFINITY ? l * exp2f(m - M) : 0.f);
+  return make_float2(M, L);
+}
+
+// 1 / (sum of exp2) of a row, 0 for an empty row.
+__device__ __forceinline__ float softmax_inv_sum(float L) { return L > 0.f ? 1.f / L : 0.f; }
+
+// Normalised weight of a log2-unit logit v given the row's max and 1 / (sum of exp2); 0 for
+// a slot that is not a candidate (v = -inf) or an empty row.
+__device__ __forceinline__ float softmax_weight(float v, float M, float inv_l) {
+  return v > -INFINITY ? exp2f(v - M) * inv_l : 0.f;
+}
+
 // ---- number formats -------------------------------------------------------------------
 
 __device__ __forceinline__ float h2f(uint16_t bits) {

@@ -45,14 +45,21 @@ hipError_t launch_append_keys(const Layout& L, const void* k_cache, const int32_
                               uint8_t* codes, void* meta, void* minmax, hipStream_t s);
 hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
                                int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s);
+// With normalize false the weights are left as logits (-inf off the candidates) and the
+// per-chunk (max, sum of exp) pairs stay at the start of ws, estimate_chunks per query head.
 hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes, const void* meta,
                            const int32_t* cand_pages, const int32_t* cand_count,
                            int cand_stride_pages, float sm_scale, float* weights, void* ws,
-                           hipStream_t s);
+                           hipStream_t s, bool normalize = true);
+int estimate_chunks(const Layout& L, int cand_stride_pages);
+// With norm given, weights hold the estimate's logits and norm its per-chunk (max, sum of
+// exp) pairs (norm_chunks per query head); the top-p kernel normalises them itself. Only
+// valid where topp_can_normalize holds (no separate group-mean pass).
 hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* cand_pages,
                        const int32_t* cand_count, int cand_stride_pages, float p,
                        int32_t* kept, int32_t* kept_count, float* tau, void* ws,
-                       hipStream_t s);
+                       hipStream_t s, const float2* norm = nullptr, int norm_chunks = 0);
+bool topp_can_normalize(const Layout& L, int cand_stride_pages);
 hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* kept,
                                 const int32_t* kept_count, int kept_stride, float sm_scale,

@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 from . import (PAGE_SIZE, make_layout, quest_page_bounds, quest_select_pages,
-               twilight_append_keys, twilight_estimate_weights, twilight_quantize_keys,
+               twilight_append_keys, twilight_estimate_topp, twilight_estimate_topp_headwise,
+               twilight_estimate_weights, twilight_quantize_keys,
                twilight_sparse_decode, twilight_sparse_decode_headwise, twilight_topp_select,
                twilight_topp_select_headwise, twilight_workspace_size)
 
@@ -145,11 +146,13 @@ def alloc_step(c: DeviceCache, headwise: bool = False) -> StepBuffers:
 
 def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[float] = None,
              stream=None, stages=("select", "estimate", "topp", "decode"),
-             append: bool = False, headwise: bool = False) -> None:
+             append: bool = False, headwise: bool = False, fused: bool = True) -> None:
     """One decode step of the hot path on `stream` (no host synchronization). With
     append, the step first maintains the caches for each sequence's newest token; with
     headwise (buffers from alloc_step(c, headwise=True)), top-p and decode keep one set per
-    query head instead of one per KV head."""
+    query head instead of one per KV head. With fused (the default), a step that runs both
+    the estimate and top-p makes the single call that lets top-p normalise the estimate's
+    logits itself; buf.weights then holds scratch, not the normalised weights."""
     if sm_scale is None:
         sm_scale = default_sm_scale(c.d)
     if append:
@@ -161,14 +164,20 @@ def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[floa
                            buf.workspace, stream=stream)
     cand_pages = buf.sel_pages if c.budget is not None else None
     cand_count = buf.sel_count if c.budget is not None else None
-    if "estimate" in stages:
-        twilight_estimate_weights(lay, c.q, c.k_codes, c.k_meta, cand_pages, cand_count, stride,
-                                  sm_scale, buf.weights, buf.workspace, stream=stream)
     topp = twilight_topp_select_headwise if headwise else twilight_topp_select
     decode = twilight_sparse_decode_headwise if headwise else twilight_sparse_decode
-    if "topp" in stages:
-        topp(lay, buf.weights, cand_pages, cand_count, stride, p, buf.kept, buf.kept_count,
-             buf.tau, buf.workspace, stream=stream)
+    if fused and "estimate" in stages and "topp" in stages:
+        both = twilight_estimate_topp_headwise if headwise else twilight_estimate_topp
+        both(lay, c.q, c.k_codes, c.k_meta, cand_pages, cand_count, stride, sm_scale, p,
+             buf.weights, buf.kept, buf.kept_count, buf.tau, buf.workspace, stream=stream)
+    else:
+        if "estimate" in stages:
+            twilight_estimate_weights(lay, c.q, c.k_codes, c.k_meta, cand_pages, cand_count,
+                                      stride, sm_scale, buf.weights, buf.workspace,
+                                      stream=stream)
+        if "topp" in stages:
+            topp(lay, buf.weights, cand_pages, cand_count, stride, p, buf.kept, buf.kept_count,
+                 buf.tau, buf.workspace, stream=stream)
     if "decode" in stages:
         decode(lay, c.q, c.k_cache, c.v_cache, buf.kept, buf.kept_count, stride * PAGE_SIZE,
                sm_scale, buf.out, buf.workspace, stream=stream)

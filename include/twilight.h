@@ -163,6 +163,33 @@ int twilight_topp_select(const twl_layout_t* L, const float* weights,
                          int32_t* kept_count, float* tau, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+/* twilight_estimate_weights followed by twilight_topp_select (or, for the _headwise form,
+ * twilight_topp_select_headwise), as one call with identical kept sets, counts and tau.
+ * The top-p kernel normalises the estimate's logits itself from their per-chunk
+ * (max, sum of exp) pairs, with the same arithmetic as the estimate's normalising pass, so
+ * that pass (a launch and a round trip of the weights) drops out of the decode step
+ * (atlas.scime.ai "Limitations": the estimate's own cost is what limits the gain when
+ * loading tokens is not the bottleneck). Shapes whose top-p needs its separate group-mean
+ * pass run the three kernels unfused, with the same results.
+ *   weights : fp32 [B, Hq, cand_stride_pages * 16], scratch for the call; afterwards it
+ *             holds either the logits or the normalised weights, so read it only through
+ *             twilight_estimate_weights.
+ * The other arguments are those of the two calls; the workspace must be as large as both
+ * need (twilight_workspace_size covers it). */
+int twilight_estimate_topp(const twl_layout_t* L, const void* q, const uint8_t* k_codes,
+                           const void* k_meta, const int32_t* cand_pages,
+                           const int32_t* cand_count, int32_t cand_stride_pages,
+                           float sm_scale, float p, float* weights, int32_t* kept,
+                           int32_t* kept_count, float* tau, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+int twilight_estimate_topp_headwise(const twl_layout_t* L, const void* q,
+                                    const uint8_t* k_codes, const void* k_meta,
+                                    const int32_t* cand_pages, const int32_t* cand_count,
+                                    int32_t cand_stride_pages, float sm_scale, float p,
+                                    float* weights, int32_t* kept, int32_t* kept_count,
+                                    float* tau, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 /* Head-wise top-p under GQA (atlas.scime.ai "Limitations": under GQA the pages' dynamic
  * budgets are per group, not per head, which costs adaptivity; this is the per-head form).
  * Each query head h is its own unit: the rule of twilight_topp_select with G = 1, applied to

@@ -24,6 +24,16 @@ def _host(buf):
             for k, v in vars(buf).items() if k != "workspace"}
 
 
+def _step(pl, c, buf, p, fused):
+    """One step; with fused, the single estimate + top-p call (weights are then scratch)."""
+    pl.run_step(c, buf, p, fused=fused)
+    torch.cuda.synchronize()
+    out = _host(buf)
+    if fused:
+        out["weights"] = None
+    return out
+
+
 def _check_all(w, out, p):
     orc = parity.oracle_units(w, p)
     sm = parity.sm_scale_for(w.spec.d)
@@ -34,7 +44,9 @@ def _check_all(w, out, p):
             cnt = int(out["sel_count"][b, g])
             assert cnt == len(res["sel"])
             assert np.array_equal(out["sel_pages"][b, g, :cnt], res["sel"])
-        parity.check_weights(out["weights"][b, g * G:(g + 1) * G], res["weights"], res["valid"])
+        if out["weights"] is not None:  # None after a fused estimate + top-p (scratch)
+            parity.check_weights(out["weights"][b, g * G:(g + 1) * G], res["weights"],
+                                 res["valid"])
         kc = int(out["kept_count"][b, g])
         kept = out["kept"][b, g, :kc]
         if n == 0:
@@ -47,17 +59,16 @@ def _check_all(w, out, p):
     return orc
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("p", [0.85, 1.0])
-def test_empty_short_and_fully_covered_sequences(p):
+def test_empty_short_and_fully_covered_sequences(p, fused):
     pl = _pipeline()
     print(f"\n[edge] empty/short sequences p={p}", flush=True)
     w = workloads.make_workload(4, B=4, seq_lens=[0, 1, 37, 700], budget=8, Hq=8, Hkv=8)
     c = pl.upload(w)
     c.build_caches()
     buf = pl.alloc_step(c)
-    pl.run_step(c, buf, p)
-    torch.cuda.synchronize()
-    out = _host(buf)
+    out = _step(pl, c, buf, p, fused)
     orc = _check_all(w, out, p)
     assert int(out["sel_count"][2, 0]) == 3                 # 37 tokens -> 3 pages, all kept
     if p == 1.0:
@@ -65,16 +76,15 @@ def test_empty_short_and_fully_covered_sequences(p):
             assert int(out["kept_count"][b, g]) == min(int(w.seq_lens[b]), 8 * 16) or b == 3
 
 
-def test_gqa_group_of_eight_and_d64():
+@pytest.mark.parametrize("fused", [False, True])
+def test_gqa_group_of_eight_and_d64(fused):
     pl = _pipeline()
     print("\n[edge] G=8, d=64", flush=True)
     w = workloads.make_workload(3, n=3000, budget=40, Hq=16, Hkv=2, d=64)
     c = pl.upload(w)
     c.build_caches()
     buf = pl.alloc_step(c)
-    pl.run_step(c, buf, 0.9)
-    torch.cuda.synchronize()
-    _check_all(w, _host(buf), 0.9)
+    _check_all(w, _step(pl, c, buf, 0.9, fused), 0.9)
 
 
 def test_single_kept_token_returns_v_exactly():
@@ -116,9 +126,7 @@ def test_exact_quest_ties_break_by_page_index():
         c.budget = budget
         buf = pl.alloc_step(c)
         w2 = workloads.Workload(**{**vars(w), "budget": budget})
-        pl.run_step(c, buf, 0.85)
-        torch.cuda.synchronize()
-        _check_all(w2, _host(buf), 0.85)
+        _check_all(w2, _step(pl, c, buf, 0.85, budget == 3), 0.85)
 
 
 def test_graph_replay_matches_eager():

@@ -37,7 +37,7 @@ def test_full_size_step(name):
     c.build_caches()
     buf = pipeline.alloc_step(c)
     print(f"[full size] {name}: running the step", flush=True)
-    pipeline.run_step(c, buf, p)
+    pipeline.run_step(c, buf, p, fused=False)
     torch.cuda.synchronize()
     kept_count = buf.kept_count.cpu().numpy()
     kept = buf.kept.cpu().numpy()

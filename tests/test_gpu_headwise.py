@@ -37,10 +37,19 @@ def _steps(w, p):
     c.build_caches()
     group = pipeline.alloc_step(c)
     head = pipeline.alloc_step(c, headwise=True)
-    pipeline.run_step(c, group, p)
+    head_sep = pipeline.alloc_step(c, headwise=True)
+    pipeline.run_step(c, group, p, fused=False)
     pipeline.run_step(c, head, p, headwise=True)
+    pipeline.run_step(c, head_sep, p, headwise=True, fused=False)
     torch.cuda.synchronize()
-    return _host(group), _host(head)
+    hw, sep = _host(head), _host(head_sep)
+    # the fused head-wise call (top-p normalising for itself) equals the separate calls
+    for key in ("kept_count", "tau", "out"):
+        assert np.array_equal(hw[key].view(np.uint8), sep[key].view(np.uint8)), key
+    for u in np.ndindex(hw["kept_count"].shape):
+        k = int(hw["kept_count"][u])
+        assert np.array_equal(hw["kept"][u][:k], sep["kept"][u][:k]), u
+    return _host(group), sep
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -97,7 +106,7 @@ def test_headwise_full_size_llama_gqa_128k():
     c = pipeline.upload(w)
     c.build_caches()
     buf = pipeline.alloc_step(c, headwise=True)
-    pipeline.run_step(c, buf, p, headwise=True)
+    pipeline.run_step(c, buf, p, headwise=True, fused=False)
     torch.cuda.synchronize()
     out = _host(buf)
     del c, buf

@@ -38,13 +38,15 @@ CASES = {
 
 
 def _run(w, p, repeat=1, key_bits=4):
+    """Run i uses the separate estimate and top-p calls (so that the normalised weights
+    can be checked) when i is even, the single fused call when i is odd."""
     from adaptive_top_sparse_amd import pipeline
     c = pipeline.upload(w, key_bits=key_bits)
     c.build_caches()
     buf = pipeline.alloc_step(c)
     outs = []
-    for _ in range(repeat):
-        pipeline.run_step(c, buf, p)
+    for i in range(repeat):
+        pipeline.run_step(c, buf, p, fused=(i % 2 == 1))
         torch.cuda.synchronize()
         outs.append({k: (None if v is None else v.cpu().numpy().copy())
                      for k, v in vars(buf).items() if k != "workspace"})
@@ -140,9 +142,16 @@ def test_sparse_decode(case):
     print(f"[{case['name']}] worst decode err {worst[0]:.2e}, end-to-end {worst[1]:.2e}")
 
 
-def test_repeat_is_bit_identical(case):
+def test_fused_estimate_topp_repeats_the_separate_calls_bit_for_bit(case):
+    """The second run makes the fused estimate + top-p call, whose top-p normalises the
+    logits itself: selection, kept sets, tau and outputs must equal the separate calls'."""
     a, b = case["out"], case["out2"]
     for key in a:
-        if a[key] is None:
+        if a[key] is None or key == "weights":   # the fused call leaves weights as scratch
+            continue
+        if key == "kept":
+            for u in np.ndindex(a["kept_count"].shape):
+                k = int(a["kept_count"][u])
+                assert np.array_equal(a["kept"][u][:k], b["kept"][u][:k]), u
             continue
         assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
