@@ -124,10 +124,30 @@ template <int G>
 __global__ __launch_bounds__(kMeanThreads) void topp_mean_kernel(
     const float* __restrict__ weights, const int32_t* __restrict__ cand_pages,
     const int32_t* __restrict__ cand_count, int cand_stride_pages,
-    const int32_t* __restrict__ seq_lens, int Hkv, int max_pages, float* __restrict__ stage) {
+    const int32_t* __restrict__ seq_lens, int Hkv, int max_pages, float* __restrict__ stage,
+    const float2* __restrict__ norm, int norm_chunks) {
+  __shared__ float s_norm[2][G];
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const long unit = static_cast<long>(b) * Hkv + g;
+  // with norm given, weights hold logits: each head's max and 1 / (sum of exp2) first, by
+  // the same wave merge as the estimate's normalising pass
+  float nM[G], nL[G];
+  if (norm != nullptr) {
+    for (int h = threadIdx.x / kWave; h < G; h += kMeanThreads / kWave) {
+      const float2 ml = merge_max_sum_wave(norm + (unit * G + h) * norm_chunks, norm_chunks);
+      if (lane_id() == 0) {
+        s_norm[0][h] = ml.x;
+        s_norm[1][h] = ml.y;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      nM[h] = s_norm[0][h];
+      nL[h] = softmax_inv_sum(s_norm[1][h]);
+    }
+  }
   const int n = seq_len_clamped(seq_lens, b, max_pages);
   const int n_slots = cand_stride_pages * kPage;
   const int32_t* cand_row = cand_pages ? cand_pages + unit * cand_stride_pages : nullptr;
@@ -142,6 +162,12 @@ __global__ __launch_bounds__(kMeanThreads) void topp_mean_kernel(
     float x[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h) load_vec<4>(row0 + static_cast<long>(h) * n_slots + sl, x[h]);
+    if (norm != nullptr) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[h][j] = softmax_weight(x[h][j], nM[h], nL[h]);
+    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -520,7 +546,8 @@ void launch_mean(const ToppArgs& a) {
   const dim3 grid((n_slots + kMeanSlots - 1) / kMeanSlots, a.L->Hkv, a.L->B);
   topp_mean_kernel<G><<<grid, kMeanThreads, 0, a.s>>>(a.weights, a.cand_pages, a.cand_count,
                                                       a.stride, a.L->seq_lens, a.L->Hkv,
-                                                      a.L->max_pages, a.stage);
+                                                      a.L->max_pages, a.stage, a.norm,
+                                                      a.norm_chunks);
 }
 
 int block_threads(int n_slots) { return n_slots <= kSmallUnit ? 256 : 1024; }
@@ -562,10 +589,6 @@ void launch_spt(const ToppArgs& a) {
 
 }  // namespace
 
-bool topp_can_normalize(const Layout& L, int cand_stride_pages) {
-  return !uses_mean_pass(L.unit_G(), cand_stride_pages * kPage);
-}
-
 size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages) {
   const long n_slots = static_cast<long>(cand_stride_pages) * kPage;
   if (!uses_mean_pass(L.unit_G(), static_cast<int>(n_slots))) return 0;
@@ -575,10 +598,13 @@ size_t topp_workspace_bytes(const Layout& L, int cand_stride_pages) {
 hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* cand_pages,
                        const int32_t* cand_count, int cand_stride_pages, float p,
                        int32_t* kept, int32_t* kept_count, float* tau, void* ws,
-                       hipStream_t s, const float2* norm, int norm_chunks) {
+                       hipStream_t s, const float2* norm, int norm_chunks,
+                       size_t stage_offset) {
   const ToppArgs a{&L, weights, cand_pages, cand_count, cand_stride_pages, p, kept,
-                   kept_count, tau, static_cast<float*>(stage_scratch(ws, L)), s, norm,
-                   norm_chunks};
+                   kept_count, tau,
+                   reinterpret_cast<float*>(static_cast<char*>(stage_scratch(ws, L)) +
+                                            stage_offset),
+                   s, norm, norm_chunks};
   const int n_slots = cand_stride_pages * kPage;
 #if TWL_TOPP_SMALL_UNIT > 0
   if (block_threads(n_slots) == 256) {

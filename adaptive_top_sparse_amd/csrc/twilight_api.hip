@@ -54,7 +54,7 @@ size_t workspace_mode(const Layout& L, int cand_stride_pages) {
   const size_t d = twl::decode_workspace_bytes(L, cand_stride_pages * twl::kPage);
   const size_t t = twl::topp_workspace_bytes(L, cand_stride_pages);
   if (e > need) need = e;
-  if (t > need) need = t;
+  if (e + t > need) need = e + t;  // the fused estimate + top-p holds both at once
   if (d > need) need = d;
   return need;
 }
@@ -261,21 +261,19 @@ int estimate_topp(bool headwise, const twl_layout_t* L, const void* q, const uin
   if (static_cast<int64_t>(cand_stride_pages) * twl::kPage > twl::kToppMaxSlots)
     return TWL_ERR_UNSUPPORTED;
   if (empty) return TWL_OK;
-  size_t need = twl::estimate_workspace_bytes(lay, cand_stride_pages);
-  const size_t need_t = twl::topp_workspace_bytes(lay, cand_stride_pages);
-  if (need_t > need) need = need_t;
-  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
+  // the estimate's chunk pairs at the start of the workspace, any group-mean stage after
+  const size_t pairs = twl::estimate_workspace_bytes(lay, cand_stride_pages);
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < pairs + twl::topp_workspace_bytes(lay, cand_stride_pages))
     return TWL_ERR_WORKSPACE;
-  // the top-p normalises the logits itself unless a separate group-mean pass is needed
-  const bool fuse = twl::topp_can_normalize(lay, cand_stride_pages);
   hipError_t e = twl::launch_estimate(lay, q, k_codes, k_meta, cand_pages, cand_count,
                                       cand_stride_pages, sm_scale, weights, workspace, stream,
-                                      !fuse);
+                                      false);
   if (e != hipSuccess) return TWL_ERR_LAUNCH;
   return launch_status(twl::launch_topp(
       lay, weights, cand_pages, cand_count, cand_stride_pages, p, kept, kept_count, tau,
-      workspace, stream, fuse ? static_cast<const float2*>(workspace) : nullptr,
-      fuse ? twl::estimate_chunks(lay, cand_stride_pages) : 0));
+      workspace, stream, static_cast<const float2*>(workspace),
+      twl::estimate_chunks(lay, cand_stride_pages), pairs));
 }
 
 int twilight_topp_select(const twl_layout_t* L, const float* weights, const int32_t* cand_pages,

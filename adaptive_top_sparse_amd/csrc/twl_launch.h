@@ -52,14 +52,15 @@ hipError_t launch_estimate(const Layout& L, const void* q, const uint8_t* codes,
                            int cand_stride_pages, float sm_scale, float* weights, void* ws,
                            hipStream_t s, bool normalize = true);
 int estimate_chunks(const Layout& L, int cand_stride_pages);
-// With norm given, weights hold the estimate's logits and norm its per-chunk (max, sum of
-// exp) pairs (norm_chunks per query head); the top-p kernel normalises them itself. Only
-// valid where topp_can_normalize holds (no separate group-mean pass).
+// With norm given, weights hold the estimate's logits (log2 units) and norm its per-chunk
+// (max, sum of exp2) pairs (norm_chunks per query head); the top-p kernels normalise them
+// themselves. The group-mean stage, when one is needed, starts stage_offset bytes into ws
+// (past the pairs, when they live there too).
 hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* cand_pages,
                        const int32_t* cand_count, int cand_stride_pages, float p,
                        int32_t* kept, int32_t* kept_count, float* tau, void* ws,
-                       hipStream_t s, const float2* norm = nullptr, int norm_chunks = 0);
-bool topp_can_normalize(const Layout& L, int cand_stride_pages);
+                       hipStream_t s, const float2* norm = nullptr, int norm_chunks = 0,
+                       size_t stage_offset = 0);
 hipError_t launch_sparse_decode(const Layout& L, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* kept,
                                 const int32_t* kept_count, int kept_stride, float sm_scale,

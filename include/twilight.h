@@ -169,8 +169,8 @@ int twilight_topp_select(const twl_layout_t* L, const float* weights,
  * (max, sum of exp) pairs, with the same arithmetic as the estimate's normalising pass, so
  * that pass (a launch and a round trip of the weights) drops out of the decode step
  * (atlas.scime.ai "Limitations": the estimate's own cost is what limits the gain when
- * loading tokens is not the bottleneck). Shapes whose top-p needs its separate group-mean
- * pass run the three kernels unfused, with the same results.
+ * loading tokens is not the bottleneck). Where top-p first forms group means over many
+ * work-groups (large GQA units), that pass normalises instead.
  *   weights : fp32 [B, Hq, cand_stride_pages * 16], scratch for the call; afterwards it
  *             holds either the logits or the normalised weights, so read it only through
  *             twilight_estimate_weights.
