@@ -115,8 +115,9 @@ def stage_bytes(c, buf, d):
     if c.budget is not None:
         out["quest_select_pages"] = int(pages.sum() * Hkv * (2 * d * 2) + qo + sel_count.sum() * 4)
     int4_row = d // 2 + (d // 32) * 4
-    out["twilight_estimate_weights"] = int(cand.sum() * int4_row + cand.sum() * G * 4 + qo)
-    out["twilight_topp_select"] = int(cand.sum() * G * 4 + kept.sum() * 4)
+    # the estimate's logits are written once and read once by the top-p
+    out["twilight_estimate_topp"] = int(cand.sum() * int4_row + cand.sum() * G * 8 + qo +
+                                        kept.sum() * 4)
     out["twilight_sparse_decode"] = int(kept.sum() * (2 * d * 2 + 4) + 2 * qo)
     return out, int(cand.sum()), int(kept.sum())
 
@@ -429,10 +430,12 @@ def main():
     torch.cuda.synchronize()
 
     # plain launches, with events around every ABI call to time the stages
+    # (the step makes the fused estimate + top-p call, so it is timed as one)
     names = (["quest_select_pages"] if base.budget is not None else []) + [
-        "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode"]
-    stage_map = {"quest_select_pages": "select", "twilight_estimate_weights": "estimate",
-                 "twilight_topp_select": "topp", "twilight_sparse_decode": "decode"}
+        "twilight_estimate_topp", "twilight_sparse_decode"]
+    stage_map = {"quest_select_pages": ("select",),
+                 "twilight_estimate_topp": ("estimate", "topp"),
+                 "twilight_sparse_decode": ("decode",)}
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -442,7 +445,7 @@ def main():
             r = i % len(reps)
             evs[i][0].record(stream)
             for j, nm in enumerate(names):
-                pipeline.run_step(reps[r], bufs[r], p, stream=stream, stages=(stage_map[nm],))
+                pipeline.run_step(reps[r], bufs[r], p, stream=stream, stages=stage_map[nm])
                 evs[i][j + 1].record(stream)
     torch.cuda.synchronize()
     t_plain = (time.perf_counter() - t_plain0) / args.steps
