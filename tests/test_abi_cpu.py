@@ -99,6 +99,38 @@ def test_invalid_arguments_are_rejected_on_the_host():
                  ctypes.c_float(0.1), FAKE, ws, wsn, None) == twl.TWL_ERR_INVALID_ARG
 
 
+def test_newer_entry_points_reject_invalid_arguments_on_the_host():
+    L = layout()
+    Lp = ctypes.byref(L)
+    ws, wsn = FAKE + (1 << 20), 1 << 30
+    f = ctypes.c_float
+    # append: token_begin is required, page_minmax may be null but must be aligned
+    assert _call("twilight_append_keys", Lp, FAKE, None, FAKE, FAKE, None, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("twilight_append_keys", Lp, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) == twl.TWL_ERR_INVALID_ARG
+    # fused estimate + top-p: required outputs, p range, scale, workspace
+    for name in ("twilight_estimate_topp", "twilight_estimate_topp_headwise"):
+        assert _call(name, Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 64, f(0.1), f(0.9), FAKE, None, FAKE,
+                     None, ws, wsn, None) == twl.TWL_ERR_INVALID_ARG
+        assert _call(name, Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 64, f(0.1), f(1.5), FAKE, FAKE, FAKE,
+                     None, ws, wsn, None) == twl.TWL_ERR_INVALID_ARG
+        assert _call(name, Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 64, f(float("nan")), f(0.9), FAKE,
+                     FAKE, FAKE, None, ws, wsn, None) == twl.TWL_ERR_INVALID_ARG
+        assert _call(name, Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 64, f(0.1), f(0.9), FAKE, FAKE, FAKE,
+                     None, None, 0, None) == twl.TWL_ERR_WORKSPACE
+        assert _call(name, Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 64, f(0.1), f(0.9), FAKE, FAKE, FAKE,
+                     None, ws, 16, None) == twl.TWL_ERR_WORKSPACE
+    # head-wise top-p and decode: same checks as the group-wise calls
+    assert _call("twilight_topp_select_headwise", Lp, FAKE, FAKE, FAKE, 64, f(0.0), FAKE, FAKE,
+                 None, ws, wsn, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("twilight_sparse_decode_headwise", Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 1024,
+                 f(0.1), FAKE, ws, 16, None) == twl.TWL_ERR_WORKSPACE
+    # key width: only 4 (or 0 for 4) and 2
+    bad = layout()
+    bad.key_bits = 3
+    assert _call("twilight_quantize_keys", ctypes.byref(bad), FAKE, None, FAKE, FAKE, None) == twl.TWL_ERR_UNSUPPORTED
+    assert twl.twilight_workspace_size(bad, 64) == 0
+
+
 def test_unsupported_shapes_are_reported():
     for bad in (layout(d=256), layout(Hq=48, Hkv=8), layout(ps=8)):
         st = _call("twilight_quantize_keys", ctypes.byref(bad), FAKE, None, FAKE, FAKE, None)
