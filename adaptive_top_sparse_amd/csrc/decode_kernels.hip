@@ -39,12 +39,19 @@ namespace {
 #define TWL_DEC_TARGET_BLOCKS 2048
 #endif
 #ifndef TWL_DEC_MAX_BATCHES
-#define TWL_DEC_MAX_BATCHES 4
+#define TWL_DEC_MAX_BATCHES 16
+#endif
+// A full-length kept list still splits into at least this many chunks.
+#ifndef TWL_DEC_MIN_CHUNKS
+#define TWL_DEC_MIN_CHUNKS 16
 #endif
 constexpr int kDecThreads = TWL_DEC_THREADS;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kDecUnroll = TWL_DEC_UNROLL;
-constexpr int kMergeSlice = 16;  // channels per merge work-group
+#ifndef TWL_MERGE_SLICE
+#define TWL_MERGE_SLICE 32
+#endif
+constexpr int kMergeSlice = TWL_MERGE_SLICE;  // channels per merge work-group
 
 // Kept tokens one work-group takes per batch: every wave takes kDecUnroll rows per lane
 // group, 64 / (D/8) lane groups per wave.
@@ -336,7 +343,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 }
 
 // Merge of the chunk partials when they are more than one: one wave per (sequence, query
-// head, 16-channel slice). Lane i takes chunks i, i + 64, ... with a running (max, sum, o)
+// head, 32-channel slice: a whole 128-byte line of each chunk's record). Lane i takes chunks i, i + 64, ... with a running (max, sum, o)
 // of its own; the lanes are then combined on the common maximum. The (max, sum) pairs sit
 // in their own compact array and each chunk's o in a 512-byte record, so every byte of the
 // partials is fetched once.
@@ -422,13 +429,18 @@ void decode_dispatch_g(const Layout& L, const void* q, const void* k, const void
 
 int decode_chunk_tokens(const Layout& L, int kept_stride) {
   // about TWL_DEC_TARGET_BLOCKS work-groups over the largest possible kept lists: one to
-  // TWL_DEC_MAX_BATCHES batches per work-group
+  // TWL_DEC_MAX_BATCHES batches per work-group, but a full-length list still in at least
+  // TWL_DEC_MIN_CHUNKS chunks, so that lists only partly full (short sequences, strong
+  // pruning) keep several work-groups each. Long lists then take long chunks: fewer
+  // partials to write and merge.
   const long units = static_cast<long>(L.B) * L.units();
   const long want =
       (static_cast<long>(kept_stride) * units + TWL_DEC_TARGET_BLOCKS - 1) / TWL_DEC_TARGET_BLOCKS;
   const int batch = decode_batch_tokens(L.d);
   long c = batch;
-  while (c < want && c < static_cast<long>(batch) * TWL_DEC_MAX_BATCHES) c <<= 1;
+  while (c < want && c < static_cast<long>(batch) * TWL_DEC_MAX_BATCHES &&
+         2 * c * TWL_DEC_MIN_CHUNKS <= kept_stride)
+    c <<= 1;
   return static_cast<int>(c);
 }
 
