@@ -70,9 +70,12 @@ __device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f
 // id, page-table entry, K/V row), pipelined across batches: ids two batches ahead, page
 // entries one ahead. Every load is issued unconditionally (entries past the list or the
 // sequence read a valid stand-in and are masked afterwards), so no load waits behind a
-// branch; the kept count is read alongside the first ids.
-template <int D, int G>
-__global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
+// branch; the kept count is read alongside the first ids. kSingle is the form for chunks
+// of exactly one batch: with no next batch to prefetch, the pipeline's second set of rows
+// and registers is compiled out, which leaves room for twice the resident work-groups.
+template <int D, int G, bool kSingle>
+__global__ __launch_bounds__(kDecThreads)
+__attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ kept,
@@ -121,11 +124,42 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       id[u] = krow[sl < tend ? sl : t0];
     }
   };
+  // Everything the first K/V loads depend on goes out at once, before any branch: the
+  // kept ids, the kept count, the sequence length and q, then batch 0's page entries
+  // (masked by the chunk's slot range; the list end is applied once the count is known).
   int ids0[U], ids1[U];
   load_ids(0, ids0);
-  load_ids(1, ids1);
+  if constexpr (!kSingle) load_ids(1, ids1);
   int K = kept_count[unit];
   const int n = seq_len_clamped(seq_lens, b, max_pages);
+  uint32_t qw[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q + (head0 + h) * D + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qw[h][j] = v[j];
+  }
+
+  // page entries of batch j: the token's page id (or a stand-in) and its in-page offset;
+  // slots at or past `last` are masked
+  auto load_rows = [&](int j, int last, const int (&id)[U], int (&phys)[U], int (&tok)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sl = slot_of(j, u);
+      const int t = id[u];
+      const bool ok = sl < last && t >= 0 && t < n;
+      tok[u] = ok ? t : -1;
+      phys[u] = trow[ok ? t / kPage : 0];
+    }
+  };
+  int phys0[U], tok0[U], phys1[U], tok1[U];
+  load_rows(0, tend, ids0, phys0, tok0);
+  // the page entries stay ahead of the exit tests below (the compiler would otherwise sink
+  // them past the branches, behind a wait on every load in flight)
+#pragma unroll
+  for (int u = 0; u < U; ++u) keep_loaded(phys0[u]);
+  TWL_PHASE(4);
+
   K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
   if (K == 0) {
     // empty kept set: o = 0, written by the first work-group
@@ -134,22 +168,13 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     return;
   }
   if (t0 >= K) return;
-  TWL_PHASE(4);
   const int t1 = min(K, t0 + chunk_tokens);
   const int nc = (K + chunk_tokens - 1) / chunk_tokens;
   const int n_batches = (t1 - t0 + BSTEP - 1) / BSTEP;
-
-  // page entries of batch j: the token's page id (or a stand-in) and its in-page offset
-  auto load_rows = [&](int j, const int (&id)[U], int (&phys)[U], int (&tok)[U]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int sl = slot_of(j, u);
-      const int t = id[u];
-      const bool ok = sl < t1 && t >= 0 && t < n;
-      tok[u] = ok ? t : -1;
-      phys[u] = trow[ok ? t / kPage : 0];
-    }
-  };
+  for (int u = 0; u < U; ++u)
+    if (slot_of(0, u) >= t1) tok0[u] = -1;
+
   auto row_of = [&](int phys, int tok) -> long {
     if (tok < 0 || !phys_ok(phys, num_phys)) return -1;
     return ((static_cast<long>(phys) * Hkv + kvh) * kPage + tok % kPage) * D;
@@ -166,13 +191,6 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     }
   };
 
-  uint32_t qw[G][4];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q + (head0 + h) * D + c0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qw[h][j] = v[j];
-  }
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -182,22 +200,24 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
   }
 
-  // pipeline: rows of batch 0, K/V of batch 0, rows of batch 1
-  int phys0[U], tok0[U], phys1[U], tok1[U];
-  load_rows(0, ids0, phys0, tok0);
+  // pipeline: K/V of batch 0, then the page entries of batch 1
   bool live0[U];
   u32x4 kv0[U], vv0[U];
   load_kv(phys0, tok0, live0, kv0, vv0);
   TWL_PHASE(5);
-  if (n_batches > 1) load_rows(1, ids1, phys1, tok1);
+  if constexpr (!kSingle) {
+    if (n_batches > 1) load_rows(1, t1, ids1, phys1, tok1);
+  }
 
   for (int j = 0; j < n_batches; ++j) {
     // ids of batch j + 2 and K/V of batch j + 1 go out before batch j is used
     int ids2[U];
-    if (j + 2 < n_batches) load_ids(j + 2, ids2);
     bool live1[U];
     u32x4 kv1[U], vv1[U];
-    if (j + 1 < n_batches) load_kv(phys1, tok1, live1, kv1, vv1);
+    if constexpr (!kSingle) {
+      if (j + 2 < n_batches) load_ids(j + 2, ids2);
+      if (j + 1 < n_batches) load_kv(phys1, tok1, live1, kv1, vv1);
+    }
 
     float s[U][G];
 #pragma unroll
@@ -251,20 +271,22 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       }
     }
     // rotate the pipeline
-    if (j + 2 < n_batches) {
-      int phys2[U], tok2[U];
-      load_rows(j + 2, ids2, phys2, tok2);
+    if constexpr (!kSingle) {
+      if (j + 2 < n_batches) {
+        int phys2[U], tok2[U];
+        load_rows(j + 2, t1, ids2, phys2, tok2);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          phys1[u] = phys2[u];
+          tok1[u] = tok2[u];
+        }
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        phys1[u] = phys2[u];
-        tok1[u] = tok2[u];
+        live0[u] = live1[u];
+        kv0[u] = kv1[u];
+        vv0[u] = vv1[u];
       }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      live0[u] = live1[u];
-      kv0[u] = kv1[u];
-      vv0[u] = vv1[u];
     }
   }
   TWL_PHASE(1);
@@ -405,11 +427,20 @@ void decode_launch(const Layout& L, const void* q, const void* k, const void* v,
                    const int32_t* kept, const int32_t* kept_count, int kept_stride,
                    float scale_log2, float* part_o, float2* part_ml, int n_chunks, int ch,
                    void* out, hipStream_t s) {
-  sparse_decode_kernel<D, G><<<dim3(n_chunks * L.units(), L.B), kDecThreads, 0, s>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), L.page_table, L.seq_lens, kept, kept_count, kept_stride,
-      L.units(), L.Hkv, L.max_pages, L.num_phys, scale_log2, part_o, part_ml, n_chunks, ch,
-      static_cast<uint16_t*>(out));
+  const dim3 grid(n_chunks * L.units(), L.B);
+  if (ch == decode_batch_tokens(D)) {
+    sparse_decode_kernel<D, G, true><<<grid, kDecThreads, 0, s>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), L.page_table, L.seq_lens, kept, kept_count,
+        kept_stride, L.units(), L.Hkv, L.max_pages, L.num_phys, scale_log2, part_o, part_ml,
+        n_chunks, ch, static_cast<uint16_t*>(out));
+  } else {
+    sparse_decode_kernel<D, G, false><<<grid, kDecThreads, 0, s>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), L.page_table, L.seq_lens, kept, kept_count,
+        kept_stride, L.units(), L.Hkv, L.max_pages, L.num_phys, scale_log2, part_o, part_ml,
+        n_chunks, ch, static_cast<uint16_t*>(out));
+  }
 }
 
 template <int D>

@@ -109,6 +109,10 @@ __device__ __forceinline__ int seq_len_clamped(const int32_t* seq_lens, int b, i
   return n > cap ? cap : n;
 }
 
+// Makes a loaded value count as used at this point: its load is issued (and waited for)
+// here, so the compiler cannot sink it past a later branch.
+__device__ __forceinline__ void keep_loaded(int v) { asm volatile("" ::"v"(v)); }
+
 __device__ __forceinline__ bool phys_ok(int phys, int num_phys) {
   return phys >= 0 && phys < num_phys;
 }
