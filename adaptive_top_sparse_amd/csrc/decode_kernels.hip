@@ -87,8 +87,11 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   constexpr int U = kDecUnroll;
   constexpr int STEP = TPW * U;     // tokens per wave per batch
   constexpr int BSTEP = decode_batch_tokens(D);
-  __shared__ float s_m[kDecWaves][G], s_l[kDecWaves][G];
-  __shared__ float s_acc[kDecWaves][G][D];
+  // per wave: each head's max, then the token-group sums of (l, acc[0..7]) per head,
+  // [value][channel slice] (one padding column against bank conflicts)
+  constexpr int kRedQ = (G * 9 + 3) / 4;
+  __shared__ float s_m[kDecWaves][G];
+  __shared__ float s_red[kDecWaves][4 * kRedQ][LPT + 1];
   TWL_PHASE_BEGIN(0, 32);
   TWL_PHASE(0);
   TWL_SPAN_BEGIN();
@@ -170,7 +173,8 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   if (t0 >= K) return;
   const int t1 = min(K, t0 + chunk_tokens);
   const int nc = (K + chunk_tokens - 1) / chunk_tokens;
-  const int n_batches = (t1 - t0 + BSTEP - 1) / BSTEP;
+  // (a single-batch chunk that reached this point holds at least one slot of the list)
+  const int n_batches = kSingle ? 1 : (t1 - t0 + BSTEP - 1) / BSTEP;
 #pragma unroll
   for (int u = 0; u < U; ++u)
     if (slot_of(0, u) >= t1) tok0[u] = -1;
@@ -234,7 +238,9 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
     }
     if (j == 0) TWL_PHASE(6);
     // one running max per head for the whole wave: the token groups' batch maxima are
-    // combined across groups, so every group's (l, acc) stays on the same scale
+    // combined across groups, so every group's (l, acc) stays on the same scale. Until a
+    // head has a live token its max is -inf; exponentials are then taken against 0, which
+    // gives exactly 0 for the -inf scores and the -inf old max.
     float pr[U][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -243,11 +249,12 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
       for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
       mb = across_groups<LPT>(mb, OpMax());
       const float mn = fmaxf(m[h], mb);
-      const float alpha = rescale(m[h], mn);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = j == 0 ? 0.f : exp2_unit(m[h] - mref);
       float lsum = l[h] * alpha;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        pr[u][h] = mn == -INFINITY ? 0.f : rescale(s[u][h], mn);
+        pr[u][h] = exp2_unit(s[u][h] - mref);
         lsum += pr[u][h];
       }
       l[h] = lsum;
@@ -290,73 +297,59 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
     }
   }
   TWL_PHASE(1);
-  // sum the token groups of each channel slice (same scale: m is shared by the wave)
+  // Sum the token groups of each channel slice (same scale: m is shared by the wave). The
+  // values are (l, acc[0..7]) per head; for d = 64 the two groups of a row are added first,
+  // then the four rows are summed scattered, so each row ends with a quarter of the values
+  // and writes them to LDS.
+  float x[4 * kRedQ];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    l[h] = across_groups<LPT>(l[h], OpSum());
+    x[h * 9] = l[h];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[h][c] = across_groups<LPT>(acc[h][c], OpSum());
+    for (int c = 0; c < 8; ++c) x[h * 9 + 1 + c] = acc[h][c];
   }
-  if constexpr (kDecWaves == 1) {
-    // one wave per work-group: lanes of token group 0 hold the chunk's totals
-    if (tk == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (nc == 1) {
-          const float L = l[h];
-          u32x4 o;
+  for (int k = G * 9; k < 4 * kRedQ; ++k) x[k] = 0.f;
+  if constexpr (LPT == 8) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const f16x2 pr2 = {static_cast<f16>(L > 0.f ? acc[h][2 * jj] / L : 0.f),
-                               static_cast<f16>(L > 0.f ? acc[h][2 * jj + 1] / L : 0.f)};
-            o[jj] = __builtin_bit_cast(uint32_t, pr2);
-          }
-          *reinterpret_cast<u32x4*>(out + (head0 + h) * D + c0) = o;
-        } else {
-          const long pidx = (head0 + h) * n_chunks + chunk;
-          if (sub == 0) part_ml[pidx] = make_float2(m[h], l[h]);
-          float* dst = part_o + pidx * D;
-          *reinterpret_cast<f32x4*>(dst + c0) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-          *reinterpret_cast<f32x4*>(dst + 4 + c0) =
-              f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-        }
-      }
+    for (int k = 0; k < G * 9; ++k) x[k] += dpp_f32<kRowRor8>(x[k]);
+  }
+  float y[kRedQ];
+  sum_rows_scatter<4 * kRedQ>(x, y);
+  {
+    const int row = lane / 16, col = lane % 16;
+    if (col < LPT) {
+#pragma unroll
+      for (int i = 0; i < kRedQ; ++i) s_red[wave][row * kRedQ + i][col] = y[i];
     }
-  } else {
-    if (tk == 0) {
+    if (lane == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (sub == 0) {
-          s_m[wave][h] = m[h];
-          s_l[wave][h] = l[h];
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s_acc[wave][h][c0 + c] = acc[h][c];
-      }
+      for (int h = 0; h < G; ++h) s_m[wave][h] = m[h];
     }
-    __syncthreads();
-    TWL_PHASE(2);
-    // this chunk's (M, L, A) per head, merged over the waves
-    for (int i = threadIdx.x; i < G * D; i += kDecThreads) {
-      const int h = i / D, c = i % D;
-      float M = s_m[0][h];
+  }
+  __syncthreads();
+  TWL_PHASE(2);
+  // this chunk's (M, L, A) per head, merged over the waves
+  for (int i = threadIdx.x; i < G * D; i += kDecThreads) {
+    const int h = i / D, c = i % D;
+    float M = s_m[0][h];
 #pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
-      float L = 0.f, A = 0.f;
+    for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    const float mref = M == -INFINITY ? 0.f : M;
+    float L = 0.f, A = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        const float f = rescale(s_m[w][h], M);
-        L += s_l[w][h] * f;
-        A += s_acc[w][h][c] * f;
-      }
-      if (nc == 1) {
-        const float o = L > 0.f ? A / L : 0.f;
-        out[(head0 + h) * D + c] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
-      } else {
-        const long pidx = (head0 + h) * n_chunks + chunk;
-        if (c == 0) part_ml[pidx] = make_float2(M, L);
-        part_o[pidx * D + c] = A;
-      }
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float f = exp2_unit(s_m[w][h] - mref);
+      L += s_red[w][h * 9][0] * f;
+      A += s_red[w][h * 9 + 1 + c % 8][c / 8] * f;
+    }
+    if (nc == 1) {
+      const float o = L > 0.f ? A / L : 0.f;
+      out[(head0 + h) * D + c] = __builtin_bit_cast(uint16_t, static_cast<f16>(o));
+    } else {
+      const long pidx = (head0 + h) * n_chunks + chunk;
+      if (c == 0) part_ml[pidx] = make_float2(M, L);
+      part_o[pidx * D + c] = A;
     }
   }
   TWL_PHASE(3);

@@ -242,6 +242,38 @@ __device__ __forceinline__ float across_groups(float v, Op op) {
   return v;
 }
 
+// Sum over the wave's four 16-lane rows, scattered: on return, row r (lanes 16r..16r+15)
+// holds in y[i] the four-row sum of x[r * N / 4 + i], lane by lane. Each permlane swap
+// carries two different values, so a value costs half a swap and half an add per step,
+// where an all-reduce costs a full swap, two copies and an add.
+template <int N>
+__device__ __forceinline__ void sum_rows_scatter(const float (&x)[N], float (&y)[N / 4]) {
+  static_assert(N % 4 == 0, "value count");
+  float h[N / 2];
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    // lanes 0-31 end with x[k] summed over rows {r, r ^ 2}, lanes 32-63 with x[k + N/2]
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x[k]),
+                                                    __builtin_bit_cast(int, x[k + N / 2]),
+                                                    false, false);
+    h[k] = __builtin_bit_cast(float, static_cast<int>(r[0])) +
+           __builtin_bit_cast(float, static_cast<int>(r[1]));
+  }
+#pragma unroll
+  for (int k = 0; k < N / 4; ++k) {
+    // even rows end with h[k] summed over rows {r, r ^ 1}, odd rows with h[k + N/4]
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, h[k]),
+                                                    __builtin_bit_cast(int, h[k + N / 4]),
+                                                    false, false);
+    y[k] = __builtin_bit_cast(float, static_cast<int>(r[0])) +
+           __builtin_bit_cast(float, static_cast<int>(r[1]));
+  }
+}
+
+// 2^x on the transcendental unit alone: exact for -inf (0) and within an ulp of exp2f for
+// x >= -126; below that it returns 0 where exp2f returns a denormal.
+__device__ __forceinline__ float exp2_unit(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Inclusive prefix sum over the 64 lanes: row-local Hillis-Steele shifts, then the row
 // totals carried across rows with row_bcast.
 template <typename T>
