@@ -60,7 +60,7 @@ __host__ __device__ constexpr int decode_batch_tokens(int d) {
 }
 
 __device__ __forceinline__ float rescale(float m, float M) {
-  return m == -INFINITY ? 0.f : exp2f(m - M);
+  return m == -INFINITY ? 0.f : exp2_unit(m - M);
 }
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }

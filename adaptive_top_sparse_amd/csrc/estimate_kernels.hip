@@ -303,9 +303,10 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       for (int i = 1; i < PB; ++i) bm = fmaxf(bm, s[i][hb]);
       const float mn = fmaxf(run_m[hb], bm);
       if (mn > -INFINITY) {
-        float l = run_m[hb] > -INFINITY ? run_l[hb] * exp2f(run_m[hb] - mn) : 0.f;
+        // mn is finite here, so the -inf old max and -inf scores give exactly 0
+        float l = run_l[hb] * exp2_unit(run_m[hb] - mn);
 #pragma unroll
-        for (int i = 0; i < PB; ++i) l += s[i][hb] > -INFINITY ? exp2f(s[i][hb] - mn) : 0.f;
+        for (int i = 0; i < PB; ++i) l += exp2_unit(s[i][hb] - mn);
         run_l[hb] = l;
         run_m[hb] = mn;
       }
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const float M = group_reduce<16>(run_m[hb], OpMax());
-    const float l = run_m[hb] > -INFINITY ? run_l[hb] * exp2f(run_m[hb] - M) : 0.f;
+    const float l = run_m[hb] > -INFINITY ? run_l[hb] * exp2_unit(run_m[hb] - M) : 0.f;
     const float L = group_reduce<16>(l, OpSum());
     const int h = c4 + 4 * hb;
     if (h < G && tok_in_page == 0) {
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     for (int w2 = 1; w2 < kEstWaves; ++w2) M = fmaxf(M, red_m[w2][h]);
     float L = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kEstWaves; ++w2) L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * exp2f(red_m[w2][h] - M) : 0.f;
+    for (int w2 = 0; w2 < kEstWaves; ++w2) L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * exp2_unit(red_m[w2][h] - M) : 0.f;
     partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(M, L);
   }
   TWL_PHASE(3);

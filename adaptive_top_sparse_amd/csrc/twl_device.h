@@ -492,12 +492,12 @@ __device__ __forceinline__ float2 merge_max_sum_wave(const float2* pr, int n_chu
     const float2 p = pr[i];
     if (p.x > -INFINITY) {
       const float mn = fmaxf(m, p.x);
-      l = (m > -INFINITY ? l * exp2f(m - mn) : 0.f) + p.y * exp2f(p.x - mn);
+      l = (m > -INFINITY ? l * exp2_unit(m - mn) : 0.f) + p.y * exp2_unit(p.x - mn);
       m = mn;
     }
   }
   const float M = wave_max(m);
-  const float L = wave_sum(m > -INFINITY ? l * exp2f(m - M) : 0.f);
+  const float L = wave_sum(m > -INFINITY ? l * exp2_unit(m - M) : 0.f);
   return make_float2(M, L);
 }
 
@@ -505,9 +505,12 @@ __device__ __forceinline__ float2 merge_max_sum_wave(const float2* pr, int n_chu
 __device__ __forceinline__ float softmax_inv_sum(float L) { return L > 0.f ? 1.f / L : 0.f; }
 
 // Normalised weight of a log2-unit logit v given the row's max and 1 / (sum of exp2); 0 for
-// a slot that is not a candidate (v = -inf) or an empty row.
+// a slot that is not a candidate (v = -inf) or an empty row (M = -inf, taken as 0 so that no
+// -inf - -inf arises). The exponential runs on the transcendental unit alone: weights below
+// 2^-126 / sum come out 0 instead of subnormal.
 __device__ __forceinline__ float softmax_weight(float v, float M, float inv_l) {
-  return v > -INFINITY ? exp2f(v - M) * inv_l : 0.f;
+  const float mref = M == -INFINITY ? 0.f : M;
+  return exp2_unit(v - mref) * inv_l;
 }
 
 // ---- number formats -------------------------------------------------------------------
