@@ -118,11 +118,25 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   const int32_t* krow = kept + unit * kept_stride;
   const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
 
-  // slot of this lane's row u of batch j
-  auto slot_of = [&](int j, int u) { return t0 + j * BSTEP + wave * STEP + u * TPW + tk; };
-  auto load_ids = [&](int j, int (&id)[U]) {
+  // q . k on the matrix cores when a wave's batch is one 16-token tile (d = 128): K rows then
+  // come in the MFMA operand layout, lane l holding channels 8 (l / 16) + 32 jj + [0, 8),
+  // jj = 0..3, of tile token l % 16, which is the token of row u = (l % 16) % 4 of token
+  // group (l % 16) / 4 in the V layout below. Each lane then has one more row (index U) to
+  // look up besides its U V rows.
+  constexpr bool kMfma = D == 128 && STEP == 16;
+  constexpr int NU = U + (kMfma ? 1 : 0);
+  constexpr int KX = kMfma ? 4 : U;  // K registers per lane
+  const int mrow = lane % 16;        // the lane's MFMA row: its tile token
+
+  // slot of this lane's row u of batch j (u = U: the MFMA row)
+  auto slot_of = [&](int j, int u) {
+    const int uu = u < U ? u : mrow % 4;
+    const int gg = u < U ? tk : mrow / 4;
+    return t0 + j * BSTEP + wave * STEP + uu * TPW + gg;
+  };
+  auto load_ids = [&](int j, int (&id)[NU]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int sl = slot_of(j, u);
       id[u] = krow[sl < tend ? sl : t0];
     }
@@ -130,24 +144,37 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   // Everything the first K/V loads depend on goes out at once, before any branch: the
   // kept ids, the kept count, the sequence length and q, then batch 0's page entries
   // (masked by the chunk's slot range; the list end is applied once the count is known).
-  int ids0[U], ids1[U];
+  int ids0[NU], ids1[NU];
   load_ids(0, ids0);
   if constexpr (!kSingle) load_ids(1, ids1);
   int K = kept_count[unit];
   const int n = seq_len_clamped(seq_lens, b, max_pages);
-  uint32_t qw[G][4];
+  // q: per head, this lane's 8 channels (dot2 form), or the MFMA B operand: column
+  // mrow < G is head mrow, with the same channels as the lane's K operand
+  uint32_t qw[kMfma ? 4 : G][4];
+  if constexpr (kMfma) {
+    const int hq = mrow < G ? mrow : 0;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q + (head0 + h) * D + c0);
+    for (int jj = 0; jj < 4; ++jj) {
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(q + (head0 + hq) * D + 32 * jj + 8 * (lane / 16));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qw[h][j] = v[j];
+      for (int e = 0; e < 4; ++e) qw[jj][e] = mrow < G ? v[e] : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(q + (head0 + h) * D + c0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qw[h][e] = v[e];
+    }
   }
 
   // page entries of batch j: the token's page id (or a stand-in) and its in-page offset;
   // slots at or past `last` are masked
-  auto load_rows = [&](int j, int last, const int (&id)[U], int (&phys)[U], int (&tok)[U]) {
+  auto load_rows = [&](int j, int last, const int (&id)[NU], int (&phys)[NU], int (&tok)[NU]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int sl = slot_of(j, u);
       const int t = id[u];
       const bool ok = sl < last && t >= 0 && t < n;
@@ -155,12 +182,12 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
       phys[u] = trow[ok ? t / kPage : 0];
     }
   };
-  int phys0[U], tok0[U], phys1[U], tok1[U];
+  int phys0[NU], tok0[NU], phys1[NU], tok1[NU];
   load_rows(0, tend, ids0, phys0, tok0);
   // the page entries stay ahead of the exit tests below (the compiler would otherwise sink
   // them past the branches, behind a wait on every load in flight)
 #pragma unroll
-  for (int u = 0; u < U; ++u) keep_loaded(phys0[u]);
+  for (int u = 0; u < NU; ++u) keep_loaded(phys0[u]);
   TWL_PHASE(4);
 
   K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
@@ -176,26 +203,37 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   // (a single-batch chunk that reached this point holds at least one slot of the list)
   const int n_batches = kSingle ? 1 : (t1 - t0 + BSTEP - 1) / BSTEP;
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < NU; ++u)
     if (slot_of(0, u) >= t1) tok0[u] = -1;
 
   auto row_of = [&](int phys, int tok) -> long {
     if (tok < 0 || !phys_ok(phys, num_phys)) return -1;
     return ((static_cast<long>(phys) * Hkv + kvh) * kPage + tok % kPage) * D;
   };
-  auto load_kv = [&](const int (&phys)[U], const int (&tok)[U], bool (&live)[U],
-                     u32x4 (&kv)[U], u32x4 (&vv)[U]) {
+  // V rows (and in the dot2 form K rows) at the lane's channels; in the MFMA form the K
+  // operand of the lane's tile token. Dead rows read row 0 and are masked afterwards.
+  auto load_kv = [&](const int (&phys)[NU], const int (&tok)[NU], bool (&live)[U],
+                     u32x4 (&kx)[KX], u32x4 (&vv)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const long row = row_of(phys[u], tok[u]);
       live[u] = row >= 0;
       const long r = row >= 0 ? row : 0;
-      kv[u] = *reinterpret_cast<const u32x4*>(k_cache + r + c0);
+      if constexpr (!kMfma) kx[u] = *reinterpret_cast<const u32x4*>(k_cache + r + c0);
       vv[u] = *reinterpret_cast<const u32x4*>(v_cache + r + c0);
+    }
+    if constexpr (kMfma) {
+      const long row = row_of(phys[U], tok[U]);
+      const uint16_t* kr = k_cache + (row >= 0 ? row : 0) + 8 * (lane / 16);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) kx[jj] = *reinterpret_cast<const u32x4*>(kr + 32 * jj);
     }
   };
 
+  // running softmax state: l and acc per head in the V layout; the max per head is uniform
+  // over the wave (dot2 form: m[h] in every lane; MFMA form: mh, lane column mrow = head)
   float m[G], l[G], acc[G][8];
+  float mh = -INFINITY;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
@@ -206,8 +244,8 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
 
   // pipeline: K/V of batch 0, then the page entries of batch 1
   bool live0[U];
-  u32x4 kv0[U], vv0[U];
-  load_kv(phys0, tok0, live0, kv0, vv0);
+  u32x4 kx0[KX], vv0[U];
+  load_kv(phys0, tok0, live0, kx0, vv0);
   TWL_PHASE(5);
   if constexpr (!kSingle) {
     if (n_batches > 1) load_rows(1, t1, ids1, phys1, tok1);
@@ -215,52 +253,91 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
 
   for (int j = 0; j < n_batches; ++j) {
     // ids of batch j + 2 and K/V of batch j + 1 go out before batch j is used
-    int ids2[U];
+    int ids2[NU];
     bool live1[U];
-    u32x4 kv1[U], vv1[U];
+    u32x4 kx1[KX], vv1[U];
     if constexpr (!kSingle) {
       if (j + 2 < n_batches) load_ids(j + 2, ids2);
-      if (j + 1 < n_batches) load_kv(phys1, tok1, live1, kv1, vv1);
+      if (j + 1 < n_batches) load_kv(phys1, tok1, live1, kx1, vv1);
     }
 
-    float s[U][G];
+    // weights pr[u][h] of the lane's V rows and the rescale alpha[h] of the old state.
+    // Exponentials are taken against the new max, or against 0 while a head has no live
+    // token yet, which gives exactly 0 for -inf scores and a -inf old max.
+    float pr[U][G], alpha[G];
+    if constexpr (kMfma) {
+      // S = K_tile q^T: lane l ends with the scores of tile rows 4 (l / 16) + r, r = 0..3
+      // (tokens u = r of token group l / 16, i.e. the lane's own V rows), for head l % 16
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+      for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const f16x4 a = __builtin_bit_cast(
+              f16x4, u32x2{kx0[jj][2 * hf], kx0[jj][2 * hf + 1]});
+          const f16x4 bq = __builtin_bit_cast(f16x4, u32x2{qw[jj][2 * hf], qw[jj][2 * hf + 1]});
+          sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bq, sacc, 0, 0, 0);
+        }
+      }
+      float sc[U];
+#pragma unroll
+      for (int r = 0; r < U; ++r) sc[r] = live0[r] ? sacc[r] * scale_log2 : -INFINITY;
+      float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mb = across_groups<16>(mb, OpMax());
+      const float mn = fmaxf(mh, mb);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float al = j == 0 ? 0.f : exp2_unit(mh - mref);
+      float pm[U];
+#pragma unroll
+      for (int r = 0; r < U; ++r) pm[r] = exp2_unit(sc[r] - mref);
+      mh = mn;
+      // to the V layout: lane (group tk, slice sub) takes head h's values from lane h of its
+      // row, which holds the same four tokens
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d = 0.f;
+        alpha[h] = j == 0 ? 0.f : row_bcast_f32(al, h);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          d = __builtin_amdgcn_fdot2(as_h2(qw[h][jj]), as_h2(kv0[u][jj]), d, false);
-        d = group_sum<LPT>(d);
-        s[u][h] = live0[u] ? d * scale_log2 : -INFINITY;
+        for (int u = 0; u < U; ++u) pr[u][h] = row_bcast_f32(pm[u], h);
+      }
+    } else {
+      float s[U][G];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float d = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            d = __builtin_amdgcn_fdot2(as_h2(qw[h][jj]), as_h2(kx0[u][jj]), d, false);
+          d = group_sum<LPT>(d);
+          s[u][h] = live0[u] ? d * scale_log2 : -INFINITY;
+        }
+      }
+      // one running max per head for the whole wave: the token groups' batch maxima are
+      // combined across groups, so every group's (l, acc) stays on the same scale
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mb = s[0][h];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
+        mb = across_groups<LPT>(mb, OpMax());
+        const float mn = fmaxf(m[h], mb);
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        alpha[h] = j == 0 ? 0.f : exp2_unit(m[h] - mref);
+#pragma unroll
+        for (int u = 0; u < U; ++u) pr[u][h] = exp2_unit(s[u][h] - mref);
+        m[h] = mn;
       }
     }
     if (j == 0) TWL_PHASE(6);
-    // one running max per head for the whole wave: the token groups' batch maxima are
-    // combined across groups, so every group's (l, acc) stays on the same scale. Until a
-    // head has a live token its max is -inf; exponentials are then taken against 0, which
-    // gives exactly 0 for the -inf scores and the -inf old max.
-    float pr[U][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mb = s[0][h];
+      float lsum = l[h] * alpha[h];
 #pragma unroll
-      for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
-      mb = across_groups<LPT>(mb, OpMax());
-      const float mn = fmaxf(m[h], mb);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = j == 0 ? 0.f : exp2_unit(m[h] - mref);
-      float lsum = l[h] * alpha;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        pr[u][h] = exp2_unit(s[u][h] - mref);
-        lsum += pr[u][h];
-      }
+      for (int u = 0; u < U; ++u) lsum += pr[u][h];
       l[h] = lsum;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] *= alpha;
-      m[h] = mn;
+      for (int c = 0; c < 8; ++c) acc[h][c] *= alpha[h];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -280,10 +357,10 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
     // rotate the pipeline
     if constexpr (!kSingle) {
       if (j + 2 < n_batches) {
-        int phys2[U], tok2[U];
+        int phys2[NU], tok2[NU];
         load_rows(j + 2, t1, ids2, phys2, tok2);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < NU; ++u) {
           phys1[u] = phys2[u];
           tok1[u] = tok2[u];
         }
@@ -291,10 +368,15 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         live0[u] = live1[u];
-        kv0[u] = kv1[u];
         vv0[u] = vv1[u];
       }
+#pragma unroll
+      for (int u = 0; u < KX; ++u) kx0[u] = kx1[u];
     }
+  }
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) m[h] = row_bcast_f32(mh, h);
   }
   TWL_PHASE(1);
   // Sum the token groups of each channel slice (same scale: m is shared by the wave). The

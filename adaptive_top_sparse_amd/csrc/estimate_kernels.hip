@@ -18,7 +18,6 @@ TWL_PHASE_STORAGE(estimate)
 namespace twl {
 namespace {
 
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kEstWaves = kEstChunk / kWave;  // 4
 constexpr int kEstBatch = 4;                  // candidate pages per wave per batch

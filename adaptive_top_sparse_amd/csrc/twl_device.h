@@ -92,6 +92,7 @@ constexpr int kWave = 64;
 
 typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -140,6 +141,28 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 template <int CTRL, int RM = 0xF>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, dpp_u32<CTRL, RM>(__builtin_bit_cast(uint32_t, v)));
+}
+// Lane n (0..15, a constant after unrolling) of each 16-lane row, broadcast to its row
+// (DPP row_newbcast).
+__device__ __forceinline__ float row_bcast_f32(float v, int n) {
+  switch (n) {
+    case 0: return dpp_f32<0x150>(v);
+    case 1: return dpp_f32<0x151>(v);
+    case 2: return dpp_f32<0x152>(v);
+    case 3: return dpp_f32<0x153>(v);
+    case 4: return dpp_f32<0x154>(v);
+    case 5: return dpp_f32<0x155>(v);
+    case 6: return dpp_f32<0x156>(v);
+    case 7: return dpp_f32<0x157>(v);
+    case 8: return dpp_f32<0x158>(v);
+    case 9: return dpp_f32<0x159>(v);
+    case 10: return dpp_f32<0x15A>(v);
+    case 11: return dpp_f32<0x15B>(v);
+    case 12: return dpp_f32<0x15C>(v);
+    case 13: return dpp_f32<0x15D>(v);
+    case 14: return dpp_f32<0x15E>(v);
+    default: return dpp_f32<0x15F>(v);
+  }
 }
 template <int CTRL, int RM = 0xF>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
