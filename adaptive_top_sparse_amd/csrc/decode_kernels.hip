@@ -118,12 +118,14 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   const int32_t* krow = kept + unit * kept_stride;
   const int32_t* trow = page_table + static_cast<long>(b) * max_pages;
 
-  // q . k on the matrix cores when a wave's batch is one 16-token tile (d = 128): K rows then
-  // come in the MFMA operand layout, lane l holding channels 8 (l / 16) + 32 jj + [0, 8),
-  // jj = 0..3, of tile token l % 16, which is the token of row u = (l % 16) % 4 of token
-  // group (l % 16) / 4 in the V layout below. Each lane then has one more row (index U) to
-  // look up besides its U V rows.
-  constexpr bool kMfma = D == 128 && STEP == 16;
+  // q . k on the matrix cores when a wave's batch is one 16-token tile (d = 128) and the group
+  // has at least 4 query heads: K rows then come in the MFMA operand layout, lane l holding
+  // channels 8 (l / 16) + 32 jj + [0, 8), jj = 0..3, of tile token l % 16, which is the token
+  // of row u = (l % 16) % 4 of token group (l % 16) / 4 in the V layout below. Each lane then
+  // has one more row (index U) to look up besides its U V rows. (That layout reads 64-byte
+  // pieces of 16 rows per load instead of whole rows; for one or two heads, where the dot2
+  // form costs few instructions, the whole-row loads are faster.)
+  constexpr bool kMfma = D == 128 && STEP == 16 && G >= 4;
   constexpr int NU = U + (kMfma ? 1 : 0);
   constexpr int KX = kMfma ? 4 : U;  // K registers per lane
   const int mrow = lane % 16;        // the lane's MFMA row: its tile token
