@@ -225,6 +225,10 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   }
   const double* sc = scores + unit * score_row_stride(max_pages);
   const int first = threadIdx.x * KPT;
+  // the first pass's histogram is cleared now; the barrier of the min/max reduction below
+  // orders these stores before its atomics
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) hist[i * NT + threadIdx.x] = 0;
   uint64_t key[KPT];
   uint64_t kmin = ~0ull, kmax = 0ull;
   // pairs of scores in 16-byte loads, all issued before any is used: rows are padded to an
@@ -274,14 +278,16 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
     mask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
     prefix = kmax & mask;
     if (threadIdx.x == 0) n_short = 0u;
-    [[maybe_unused]] int npass = 0;
+    int npass = 0;
     for (;;) {
       const int lo_bit = top >= 10 ? top - 10 : 0;
       const int nbits = top - lo_bit + 1;
       const uint64_t dmask = (1ull << nbits) - 1ull;
+      if (npass > 0) {
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) hist[i * NT + threadIdx.x] = 0;
-      __syncthreads();
+        for (int i = 0; i < BPT; ++i) hist[i * NT + threadIdx.x] = 0;
+        __syncthreads();
+      }
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         if (first + i < P && (key[i] & mask) == prefix)

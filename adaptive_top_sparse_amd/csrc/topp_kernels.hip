@@ -237,6 +237,11 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   const int wbase = wv * SPT * kWave;
   const float* row0 = src + unit * G * n_slots;
   const float inv_g = 1.0f / static_cast<float>(G);  // exact: G is a power of two
+  // the first pass's histogram is cleared now; the barrier of the min/max reduction that
+  // ends pass 0 orders these stores before its atomics
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) mass[i * NT + threadIdx.x] = 0ull;
+  if (threadIdx.x == 0) n_short[0] = 0u;
 
   // pass 0: W = mean of the group's weights on candidate slots (0 elsewhere). A batch of
   // vectors first issues all its loads (weights and page ids), then forms W; n_slots is a
@@ -372,10 +377,12 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       const uint32_t range = hi - lo;
       const int bits = range == 0 ? 0 : 32 - __clz(range);
       const int shift = bits > 11 ? bits - 11 : 0;
+      if (pass_no > 0) {
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) mass[i * NT + threadIdx.x] = 0ull;
-      if (threadIdx.x == 0) n_short[pass_no & 1] = 0u;
-      __syncthreads();
+        for (int i = 0; i < BPT; ++i) mass[i * NT + threadIdx.x] = 0ull;
+        if (threadIdx.x == 0) n_short[pass_no & 1] = 0u;
+        __syncthreads();
+      }
       if (pass_no == 0) TWL_PHASE(12);
       for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll
