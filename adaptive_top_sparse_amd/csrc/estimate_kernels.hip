@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   constexpr int NW = VG * BITS / 32;  // code words per lane and token
   constexpr int RB = D * BITS / 8;    // code bytes per token row
   static_assert(G <= 8, "at most 8 query heads per KV head");
-  __shared__ f16 qs[G][D];
+  __shared__ __attribute__((aligned(16))) f16 qs[G][D];
   __shared__ float qsum[G][NG];
   __shared__ float red_m[kEstWaves][G], red_l[kEstWaves][G];
   TWL_PHASE_BEGIN(0, 32);
@@ -135,29 +135,34 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   const int32_t* crow = cand_pages ? cand_pages + unit * cand_stride_pages : nullptr;
 
   auto rank_of = [&](int j, int i) { return page0 + (j * kEstWaves + wave) * PB + i; };
-  // page ids of batch j, read before the candidate count is known (from inside the row)
+  // page ids of batch j, read before the candidate count is known (from inside the row).
+  // The loads are unconditional (without a page list they read page-table entry 0 and are
+  // replaced by the rank), and the tests below use no short-circuit branches, so that the
+  // compiler issues a batch's loads together instead of one per branch.
+  const int32_t* id_src = crow != nullptr ? crow : page_table;
   auto load_ids = [&](int j, int (&pid)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int r = rank_of(j, i);
-      pid[i] = crow == nullptr ? r : crow[r < page_end ? r : page0];
+      const int v = id_src[crow != nullptr ? (r < page_end ? r : page0) : 0];
+      pid[i] = crow == nullptr ? r : v;
     }
   };
   int ids0[PB], ids1[PB];
   load_ids(0, ids0);
   load_ids(1, ids1);
-  int cnt = cand_stride_pages;
-  if (crow != nullptr) {
-    cnt = cand_count ? cand_count[unit] : (n + kPage - 1) / kPage;
-    cnt = cnt < cand_stride_pages ? cnt : cand_stride_pages;
-  }
+  // the candidate count, loaded unconditionally as well (entry 0 of the page table stands in
+  // for a missing count array) and chosen by selects, not branches
+  const int cnt_v = (cand_count != nullptr ? cand_count : page_table)[cand_count != nullptr ? unit : 0];
+  const int cnt_list = cand_count != nullptr ? cnt_v : (n + kPage - 1) / kPage;
+  const int cnt = crow == nullptr ? cand_stride_pages : min(cnt_list, cand_stride_pages);
   // validated page ids and their page-table entries
   auto load_phys = [&](int j, int (&pid)[PB], int (&phys)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int r = rank_of(j, i);
-      const bool ok = r < page_end && r < cnt && pid[i] >= 0 && pid[i] < max_pages &&
-                      pid[i] * kPage < n;
+      const bool ok = (r < page_end) & (r < cnt) & (pid[i] >= 0) & (pid[i] < max_pages) &
+                      (pid[i] * kPage < n);
       pid[i] = ok ? pid[i] : -1;
       phys[i] = page_table[static_cast<long>(b) * max_pages + (ok ? pid[i] : 0)];
     }
@@ -167,24 +172,24 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
                         uint32_t (&mw)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const bool ok = pid[i] >= 0 && phys_ok(phys[i], num_phys);
+      const bool ok = (pid[i] >= 0) & (phys[i] >= 0) & (phys[i] < num_phys);
       pid[i] = ok ? pid[i] : -1;
       const long row = ok ? (static_cast<long>(phys[i]) * Hkv + g) * kPage + tok_in_page : 0;
       cw[i] = load_words<NW>(reinterpret_cast<const uint32_t*>(codes + row * RB) + c4 * NW);
       mw[i] = meta[row * NG + c4 * VG / 32];
     }
   };
-  int phys0[PB], phys1[PB];
-  CodeWords<NW> cw0[PB];
-  uint32_t mw0[PB];
-  load_phys(0, ids0, phys0);
-  load_codes(ids0, phys0, cw0, mw0);
-  if (n_batches > 1) load_phys(1, ids1, phys1);
-
-  // the group's queries and their per-group sums
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D, c = i % D;
-    qs[h][c] = __builtin_bit_cast(f16, q[(static_cast<long>(b) * Hq + g * G + h) * D + c]);
+  // the group's queries and their per-group sums, staged while the first ids are in flight:
+  // a block barrier waits for every load the wave has issued, so it comes before the page
+  // entries and codes are requested
+  // (every thread copies one 16-byte piece, several threads the same one with the same
+  // bytes, so that no branch holds the id loads back)
+  static_assert(kEstChunk % (G * D / 8) == 0, "whole copies of q per block");
+  {
+    const int piece = threadIdx.x % (G * D / 8);
+    const int h = piece / (D / 8), c = (piece % (D / 8)) * 8;
+    *reinterpret_cast<u32x4*>(&qs[h][c]) =
+        *reinterpret_cast<const u32x4*>(q + (static_cast<long>(b) * Hq + g * G + h) * D + c);
   }
   __syncthreads();
   if (threadIdx.x < G * NG) {
@@ -194,6 +199,11 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     qsum[h][grp] = acc;
   }
   __syncthreads();
+  int phys0[PB], phys1[PB];
+  CodeWords<NW> cw0[PB];
+  uint32_t mw0[PB];
+  load_phys(0, ids0, phys0);
+
   // A operands: row (vg, h) = (lane%16 / 4, lane%16 % 4 + 4 hb), nonzero only on the
   // channels of virtual group vg and for h < G
   f16x4 qa[NHB][MPT];
@@ -220,6 +230,12 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       const int h = r + 4 * hb;
       qg[hb][r] = (h < G && adds_zero) ? qsum[h < G ? h : 0][c4 * VG / 32] : 0.f;
     }
+  // every page entry of the batch is in hand before the code loads go out (the compiler
+  // would otherwise interleave them, one round trip per page)
+#pragma unroll
+  for (int i = 0; i < PB; ++i) keep_loaded(phys0[i]);
+  load_codes(ids0, phys0, cw0, mw0);
+  if (n_batches > 1) load_phys(1, ids1, phys1);
   TWL_PHASE(1);
 
   float run_m[NHB], run_l[NHB];  // online max and sum of exp of this lane's head(s)
