@@ -127,7 +127,10 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int tok_in_page = lane % 16;
   const int c4 = lane / 16;
-  const int n = seq_len_clamped(seq_lens, b, max_pages);
+  // the sequence length comes on the vector path (made scalar after the q staging, where it
+  // is first needed), so that no kernel-argument wait also waits for it
+  const int n_lane = load_uniform_vec(seq_lens + b);
+  int n = 0;  // set after the q staging
   const int n_slots = cand_stride_pages * kPage;
   const int page0 = chunk * chunk_pages;
   const int page_end = min(cand_stride_pages, page0 + chunk_pages);
@@ -152,10 +155,11 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   load_ids(0, ids0);
   load_ids(1, ids1);
   // the candidate count, loaded unconditionally as well (entry 0 of the page table stands in
-  // for a missing count array) and chosen by selects, not branches
-  const int cnt_v = (cand_count != nullptr ? cand_count : page_table)[cand_count != nullptr ? unit : 0];
-  const int cnt_list = cand_count != nullptr ? cnt_v : (n + kPage - 1) / kPage;
-  const int cnt = crow == nullptr ? cand_stride_pages : min(cnt_list, cand_stride_pages);
+  // for a missing count array), on the vector path; it is first needed after the q staging
+  // below, whose barrier waits for it anyway
+  const int cnt_lane = load_uniform_vec((cand_count != nullptr ? cand_count : page_table) +
+                                        (cand_count != nullptr ? unit : 0));
+  int cnt = cand_stride_pages;  // set after the q staging
   // validated page ids and their page-table entries
   auto load_phys = [&](int j, int (&pid)[PB], int (&phys)[PB]) {
 #pragma unroll
@@ -199,6 +203,13 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     qsum[h][grp] = acc;
   }
   __syncthreads();
+  {
+    const int nv = __builtin_amdgcn_readfirstlane(n_lane);
+    n = nv < 0 ? 0 : (nv > max_pages * kPage ? max_pages * kPage : nv);
+    const int cnt_v = __builtin_amdgcn_readfirstlane(cnt_lane);
+    const int cnt_list = cand_count != nullptr ? cnt_v : (n + kPage - 1) / kPage;
+    cnt = crow == nullptr ? cand_stride_pages : min(cnt_list, cand_stride_pages);
+  }
   int phys0[PB], phys1[PB];
   CodeWords<NW> cw0[PB];
   uint32_t mw0[PB];

@@ -114,6 +114,17 @@ __device__ __forceinline__ int seq_len_clamped(const int32_t* seq_lens, int b, i
 // here, so the compiler cannot sink it past a later branch.
 __device__ __forceinline__ void keep_loaded(int v) { asm volatile("" ::"v"(v)); }
 
+// A load of a value that is the same for the whole wave, issued on the vector path: its
+// address depends on an opaque zero held in a VGPR. Vector loads return in order, so waiting
+// for a later load (a kernel argument, say) does not also wait for this one, as it would for
+// a scalar load, and it can be issued alongside the wave's first vector loads. The caller
+// makes the value scalar (readfirstlane) where it is needed.
+__device__ __forceinline__ int load_uniform_vec(const int32_t* p) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return p[z];
+}
+
 __device__ __forceinline__ bool phys_ok(int phys, int num_phys) {
   return phys >= 0 && phys < num_phys;
 }
