@@ -87,12 +87,14 @@ __device__ __forceinline__ void load_vec(const float* p, float (&x)[VW]) {
   }
 }
 
-// Page id behind slot s0, loaded unconditionally (entry 0 stands in when the slot's page
-// rank is past the candidates) so that loads can be issued before any is used.
-__device__ __forceinline__ int page_id_of(const int32_t* cand_row, int cnt, int s0) {
+// Page id behind slot s0, loaded unconditionally so that loads can be issued before any is
+// used (and before the candidate count is known): entry 0 stands in when the slot's page
+// rank is past the row's `bound` entries. Ranks past the candidate count read entries that
+// page_token rejects.
+__device__ __forceinline__ int page_id_of(const int32_t* cand_row, int bound, int s0) {
   if (cand_row == nullptr) return 0;
   const int r = s0 / kPage;
-  return cand_row[r < cnt ? r : 0];
+  return cand_row[r < bound ? r : 0];
 }
 
 // Logical token of slot s0 (s0 a multiple of 4 or less, so its vector stays in one page)
@@ -228,10 +230,21 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   const long unit = static_cast<long>(b) * units + g;
   // a head-wise unit (one query head) reads its KV head's candidates: cand_div = G
   const long cunit = unit / cand_div;
-  const int n = seq_len_clamped(seq_lens, b, max_pages);
   const int n_slots = cand_stride_pages * kPage;
   const int32_t* cand_row = cand_pages ? cand_pages + cunit * cand_stride_pages : nullptr;
-  const int cnt = candidate_pages(cand_pages, cand_count, cunit, cand_stride_pages, n);
+  // the sequence length and candidate count come on the vector path and are made scalar
+  // where the first batch is formed, so that neither holds up the weight loads (the page-id
+  // loads are bounded by the row's stride, not by the count)
+  const int n_lane = load_uniform_vec(seq_lens + b);
+  const int cnt_lane = load_uniform_vec(cand_count != nullptr ? cand_count + cunit : seq_lens + b);
+  int n = 0, cnt = 0;
+  auto resolve_counts = [&]() {
+    const int nv = __builtin_amdgcn_readfirstlane(n_lane);
+    n = nv < 0 ? 0 : (nv > max_pages * kPage ? max_pages * kPage : nv);
+    const int cv = __builtin_amdgcn_readfirstlane(cnt_lane);
+    const int c = cand_count != nullptr ? cv : (n + kPage - 1) / kPage;
+    cnt = cand_pages == nullptr ? 0 : (c < cand_stride_pages ? c : cand_stride_pages);
+  };
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
   const int wbase = wv * SPT * kWave;
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
 #pragma unroll
       for (int h = 0; h < G; ++h)
         load_vec<VW>(row0 + static_cast<long>(h) * n_slots + sl, x[i][h]);
-      pid[i] = page_id_of(cand_row, cnt, sl);
+      pid[i] = page_id_of(cand_row, cand_stride_pages, sl);
     }
   };
   auto finish_batch = [&](int v0, auto& x, auto& pid, float (*dst)[VW], int* t0_out) {
@@ -322,6 +335,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       int pid[kBatch];
       float w[kBatch][VW];
       load_batch(NR + v, x, pid);
+      if (v == 0) resolve_counts();
       finish_batch(NR + v, x, pid, w, nullptr);
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
@@ -339,6 +353,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     int pid[kRegBatch];
     load_batch(v, x, pid);
     if (NL == 0 && v == 0 && norm != nullptr) norm_stats();
+    if (NL == 0 && v == 0) resolve_counts();
     finish_batch(v, x, pid, W + v, kKeepT0 ? T0 + v : nullptr);
   }
   TWL_PHASE(1);
@@ -494,7 +509,8 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       const int s0 = wbase + v * kWave * VW + lane * VW;
       const int t0 = t0_known != kNoToken
                          ? t0_known
-                         : page_token(cand_row, cnt, max_pages, s0, page_id_of(cand_row, cnt, s0));
+                         : page_token(cand_row, cnt, max_pages, s0,
+                                      page_id_of(cand_row, cand_stride_pages, s0));
       uint32_t pos = run + incl - c;
 #pragma unroll
       for (int j = 0; j < VW; ++j)
