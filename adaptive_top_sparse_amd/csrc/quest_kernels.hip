@@ -212,32 +212,18 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   TWL_PHASE(4);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
-  const int n = seq_len_clamped(seq_lens, b, max_pages);
-  const int P = (n + kPage - 1) / kPage;
-  const int m = min(budget, P);
   const long unit = static_cast<long>(b) * Hkv + g;
-  int32_t* out = sel_pages + unit * budget;
-  if (threadIdx.x == 0) sel_count[unit] = m;
-  if (m == P) {
-    for (int i = threadIdx.x; i < P; i += NT) out[i] = i;
-    TWL_PHASE_FLUSH(4, 32);
-    return;
-  }
   const double* sc = scores + unit * score_row_stride(max_pages);
   const int first = threadIdx.x * KPT;
-  // the first pass's histogram is cleared now; the barrier of the min/max reduction below
-  // orders these stores before its atomics
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) hist[i * NT + threadIdx.x] = 0;
-  uint64_t key[KPT];
-  uint64_t kmin = ~0ull, kmax = 0ull;
-  // pairs of scores in 16-byte loads, all issued before any is used: rows are padded to an
-  // even stride, and pairs that start past the sequence load entry 0 instead
-  constexpr int VW = KPT < 2 ? 1 : 2;
+  // The scores are requested before the sequence length is known (bounded by the row, whose
+  // stride is even and at least max_pages), and the length comes on the vector path, so the
+  // two round trips overlap; pages past the sequence are masked below.
+  const int n_lane = load_uniform_vec(seq_lens + b);
+  constexpr int VW = KPT < 2 ? 1 : 2;  // pairs of scores in 16-byte loads
   double sv[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; i += VW) {
-    const int pl = first + i < P ? first + i : 0;
+    const int pl = first + i < max_pages ? first + i : 0;
     if constexpr (VW == 2) {
       const f64x2 v = *reinterpret_cast<const f64x2*>(sc + pl);
       sv[i] = v[0];
@@ -246,6 +232,23 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
       sv[i] = sc[pl];
     }
   }
+  const int nv = __builtin_amdgcn_readfirstlane(n_lane);
+  const int n = nv < 0 ? 0 : (nv > max_pages * kPage ? max_pages * kPage : nv);
+  const int P = (n + kPage - 1) / kPage;
+  const int m = min(budget, P);
+  int32_t* out = sel_pages + unit * budget;
+  if (threadIdx.x == 0) sel_count[unit] = m;
+  if (m == P) {
+    for (int i = threadIdx.x; i < P; i += NT) out[i] = i;
+    TWL_PHASE_FLUSH(4, 32);
+    return;
+  }
+  // the first pass's histogram is cleared now; the barrier of the min/max reduction below
+  // orders these stores before its atomics
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) hist[i * NT + threadIdx.x] = 0;
+  uint64_t key[KPT];
+  uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int p = first + i;
