@@ -28,8 +28,8 @@ EXPORTED = ("twilight_quantize_keys", "quest_page_bounds", "quest_select_pages",
             "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode",
             "twilight_append_keys", "twilight_topp_select_headwise",
             "twilight_sparse_decode_headwise", "twilight_estimate_topp",
-            "twilight_estimate_topp_headwise", "twilight_workspace_size",
-            "twilight_status_string")
+            "twilight_estimate_topp_headwise", "quest_page_scores", "quest_top_pages",
+            "quest_score_stride", "twilight_workspace_size", "twilight_status_string")
 
 
 class TwilightError(RuntimeError):
@@ -71,8 +71,12 @@ def lib():
         L.twilight_sparse_decode_headwise.argtypes = L.twilight_sparse_decode.argtypes
         L.twilight_estimate_topp.argtypes = [LP, P, P, P, P, P, I32, F, F, P, P, P, P, P, SZ, P]
         L.twilight_estimate_topp_headwise.argtypes = L.twilight_estimate_topp.argtypes
-        for name in EXPORTED[:11]:
+        L.quest_page_scores.argtypes = [LP, P, P, P, P]
+        L.quest_top_pages.argtypes = [LP, P, I32, P, P, P]
+        for name in EXPORTED[:13]:
             getattr(L, name).restype = ctypes.c_int
+        L.quest_score_stride.argtypes = [I32]
+        L.quest_score_stride.restype = ctypes.c_int64
         L.twilight_workspace_size.argtypes = [LP, I32]
         L.twilight_workspace_size.restype = ctypes.c_size_t
         L.twilight_status_string.argtypes = [ctypes.c_int]
@@ -177,6 +181,30 @@ def quest_select_pages(layout: Layout, q, page_minmax, budget_pages: int, sel_pa
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check("quest_select_pages", st)
+
+
+def quest_score_stride(max_pages_per_seq: int) -> int:
+    """Doubles per (sequence, KV head) row of a Quest score buffer."""
+    return int(lib().quest_score_stride(int(max_pages_per_seq)))
+
+
+def quest_page_scores(layout: Layout, q, page_minmax, scores, stream=None) -> None:
+    import torch
+    st = lib().quest_page_scores(
+        ctypes.byref(layout), _ptr(q, torch.float16, "q"),
+        _ptr(page_minmax, torch.float16, "page_minmax"), _ptr(scores, torch.float64, "scores"),
+        _stream(stream))
+    _check("quest_page_scores", st)
+
+
+def quest_top_pages(layout: Layout, scores, budget_pages: int, sel_pages, sel_count,
+                    stream=None) -> None:
+    import torch
+    st = lib().quest_top_pages(
+        ctypes.byref(layout), _ptr(scores, torch.float64, "scores"), int(budget_pages),
+        _ptr(sel_pages, torch.int32, "sel_pages"), _ptr(sel_count, torch.int32, "sel_count"),
+        _stream(stream))
+    _check("quest_top_pages", st)
 
 
 def twilight_estimate_weights(layout: Layout, q, k_codes, k_meta, cand_pages, cand_count,

@@ -427,9 +427,10 @@ size_t quest_workspace_bytes(const Layout& L) {
                   256);
 }
 
-hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
-                               int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s) {
-  double* scores = static_cast<double*>(stage_scratch(ws, L));
+long quest_score_stride(int max_pages) { return score_row_stride(max_pages); }
+
+hipError_t launch_quest_scores(const Layout& L, const void* q, const void* minmax, double* scores,
+                               hipStream_t s) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* mm = static_cast<const uint16_t*>(minmax);
   auto score = [&](auto d_tag, auto g_tag) {
@@ -450,8 +451,11 @@ hipError_t launch_quest_select(const Layout& L, const void* q, const void* minma
   };
   if (L.d == 128) score_d(std::integral_constant<int, 128>());
   else score_d(std::integral_constant<int, 64>());
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_quest_top(const Layout& L, const double* scores, int budget,
+                            int32_t* sel_pages, int32_t* sel_count, hipStream_t s) {
 #if TWL_SELECT_SMALL > 0
   // a tuning option, off by default: 256 threads (one wave per SIMD) up to this many pages
   if (L.max_pages <= TWL_SELECT_SMALL) {
@@ -473,6 +477,14 @@ hipError_t launch_quest_select(const Layout& L, const void* q, const void* minma
   else if (kpt <= 16) select_launch<1024, 16>(L, budget, sel_pages, sel_count, scores, s);
   else select_launch<1024, 32>(L, budget, sel_pages, sel_count, scores, s);
   return hipGetLastError();
+}
+
+hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
+                               int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s) {
+  double* scores = static_cast<double*>(stage_scratch(ws, L));
+  const hipError_t e = launch_quest_scores(L, q, minmax, scores, s);
+  if (e != hipSuccess) return e;
+  return launch_quest_top(L, scores, budget, sel_pages, sel_count, s);
 }
 
 }  // namespace twl

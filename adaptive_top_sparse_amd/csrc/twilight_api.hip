@@ -208,6 +208,38 @@ int quest_select_pages(const twl_layout_t* L, const void* q, const void* page_mi
                                                 sel_count, workspace, stream));
 }
 
+int64_t quest_score_stride(int32_t max_pages_per_seq) {
+  if (max_pages_per_seq < 1) return -1;
+  return twl::quest_score_stride(max_pages_per_seq);
+}
+
+int quest_page_scores(const twl_layout_t* L, const void* q, const void* page_minmax,
+                      double* scores, hipStream_t stream) {
+  Layout lay{};
+  bool empty = false;
+  int st = check_layout(L, &lay, &empty);
+  if (st != TWL_OK) return st;
+  if (q == nullptr || page_minmax == nullptr || scores == nullptr) return TWL_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(page_minmax) || !aligned16(scores)) return TWL_ERR_INVALID_ARG;
+  if (empty) return TWL_OK;
+  return launch_status(twl::launch_quest_scores(lay, q, page_minmax, scores, stream));
+}
+
+int quest_top_pages(const twl_layout_t* L, const double* scores, int32_t budget_pages,
+                    int32_t* sel_pages, int32_t* sel_count, hipStream_t stream) {
+  Layout lay{};
+  bool empty = false;
+  int st = check_layout(L, &lay, &empty);
+  if (st != TWL_OK) return st;
+  if (scores == nullptr || sel_pages == nullptr || sel_count == nullptr) return TWL_ERR_INVALID_ARG;
+  if (!aligned16(scores) || !aligned4(sel_pages) || !aligned4(sel_count)) return TWL_ERR_INVALID_ARG;
+  if (budget_pages < 1) return TWL_ERR_INVALID_ARG;
+  if (lay.max_pages > twl::kQuestMaxPages) return TWL_ERR_UNSUPPORTED;
+  if (empty) return TWL_OK;
+  return launch_status(
+      twl::launch_quest_top(lay, scores, budget_pages, sel_pages, sel_count, stream));
+}
+
 int twilight_estimate_weights(const twl_layout_t* L, const void* q, const uint8_t* k_codes,
                               const void* k_meta, const int32_t* cand_pages,
                               const int32_t* cand_count, int32_t cand_stride_pages,

@@ -43,6 +43,13 @@ hipError_t launch_page_bounds(const Layout& L, const void* k_cache, const int32_
                               void* minmax, hipStream_t s);
 hipError_t launch_append_keys(const Layout& L, const void* k_cache, const int32_t* token_begin,
                               uint8_t* codes, void* meta, void* minmax, hipStream_t s);
+// Quest page scores into rows of quest_score_stride(max_pages) doubles, then the top pages
+// from such rows; launch_quest_select runs both with the scores in the workspace.
+long quest_score_stride(int max_pages);
+hipError_t launch_quest_scores(const Layout& L, const void* q, const void* minmax, double* scores,
+                               hipStream_t s);
+hipError_t launch_quest_top(const Layout& L, const double* scores, int budget,
+                            int32_t* sel_pages, int32_t* sel_count, hipStream_t s);
 hipError_t launch_quest_select(const Layout& L, const void* q, const void* minmax, int budget,
                                int32_t* sel_pages, int32_t* sel_count, void* ws, hipStream_t s);
 // With normalize false the weights are left as logits (-inf off the candidates) and the

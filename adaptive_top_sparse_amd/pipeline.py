@@ -15,6 +15,7 @@ import numpy as np
 import torch
 
 from . import (PAGE_SIZE, make_layout, quest_page_bounds, quest_select_pages,
+               quest_page_scores, quest_top_pages, quest_score_stride,
                twilight_append_keys, twilight_estimate_topp, twilight_estimate_topp_headwise,
                twilight_estimate_weights, twilight_quantize_keys,
                twilight_sparse_decode, twilight_sparse_decode_headwise, twilight_topp_select,
@@ -144,6 +145,13 @@ def alloc_step(c: DeviceCache, headwise: bool = False) -> StepBuffers:
         workspace=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev))
 
 
+def quest_scores_view(c: DeviceCache, buf) -> "torch.Tensor":
+    """fp64 view [B, Hkv, quest_score_stride] of the start of the step's workspace."""
+    stride = quest_score_stride(c.max_pages)
+    n = c.B * c.Hkv * stride
+    return buf.workspace[:n * 8].view(torch.float64).view(c.B, c.Hkv, stride)
+
+
 def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[float] = None,
              stream=None, stages=("select", "estimate", "topp", "decode"),
              append: bool = False, headwise: bool = False, fused: bool = True) -> None:
@@ -162,6 +170,14 @@ def run_step(c: DeviceCache, buf: StepBuffers, p: float, sm_scale: Optional[floa
     if c.budget is not None and "select" in stages:
         quest_select_pages(lay, c.q, c.page_minmax, c.budget, buf.sel_pages, buf.sel_count,
                            buf.workspace, stream=stream)
+    if c.budget is not None and ("quest_scores" in stages or "quest_top" in stages):
+        # the same two halves as separate calls, with the scores where the combined call
+        # keeps them: the start of the workspace
+        scores = quest_scores_view(c, buf)
+        if "quest_scores" in stages:
+            quest_page_scores(lay, c.q, c.page_minmax, scores, stream=stream)
+        if "quest_top" in stages:
+            quest_top_pages(lay, scores, c.budget, buf.sel_pages, buf.sel_count, stream=stream)
     cand_pages = buf.sel_pages if c.budget is not None else None
     cand_count = buf.sel_count if c.budget is not None else None
     topp = twilight_topp_select_headwise if headwise else twilight_topp_select

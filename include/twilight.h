@@ -129,6 +129,19 @@ int quest_select_pages(const twl_layout_t* L, const void* q, const void* page_mi
                        int32_t budget_pages, int32_t* sel_pages, int32_t* sel_count,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The two halves of quest_select_pages, for callers that want the page scores themselves.
+ * quest_page_scores writes score(page) as defined above, exact in fp64, for pages
+ * [0, P_b) of every (sequence, KV head); entries at and past P_b are left untouched.
+ *   scores : fp64 [B, Hkv, quest_score_stride(max_pages_per_seq)], 16-byte aligned
+ * quest_top_pages then writes what quest_select_pages writes, from such scores (entries at
+ * and past P_b are ignored). Same limits and errors as quest_select_pages, without a
+ * workspace. The caller owns every buffer. */
+int64_t quest_score_stride(int32_t max_pages_per_seq); /* max_pages rounded up to 64; -1 if < 1 */
+int quest_page_scores(const twl_layout_t* L, const void* q, const void* page_minmax,
+                      double* scores, hipStream_t stream);
+int quest_top_pages(const twl_layout_t* L, const double* scores, int32_t budget_pages,
+                    int32_t* sel_pages, int32_t* sel_count, hipStream_t stream);
+
 /* Twilight's weight estimate over the candidates (atlas.scime.ai "Approach": top-p is
  * applied to the estimated attention weights of the pre-selected tokens, estimated with
  * the 4-bit key cache). Candidate slot j = r * 16 + o is offset o of the r-th candidate

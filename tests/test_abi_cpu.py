@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "twilight.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_six_stages_and_helpers():
@@ -124,6 +124,16 @@ def test_newer_entry_points_reject_invalid_arguments_on_the_host():
                  None, ws, wsn, None) == twl.TWL_ERR_INVALID_ARG
     assert _call("twilight_sparse_decode_headwise", Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 1024,
                  f(0.1), FAKE, ws, 16, None) == twl.TWL_ERR_WORKSPACE
+    # Quest scores and top pages on their own: required buffers, alignment, budget, size limit
+    assert _call("quest_page_scores", Lp, FAKE, FAKE, None, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("quest_page_scores", Lp, FAKE, FAKE, FAKE + 8, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("quest_top_pages", Lp, FAKE, 0, FAKE, FAKE, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("quest_top_pages", Lp, None, 64, FAKE, FAKE, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("quest_top_pages", Lp, FAKE + 8, 64, FAKE, FAKE, None) == twl.TWL_ERR_INVALID_ARG
+    big = layout(max_pages=40000)
+    assert _call("quest_top_pages", ctypes.byref(big), FAKE, 64, FAKE, FAKE, None) == twl.TWL_ERR_UNSUPPORTED
+    assert twl.quest_score_stride(1) == 64 and twl.quest_score_stride(8192) == 8192
+    assert twl.quest_score_stride(8193) == 8256 and twl.quest_score_stride(0) == -1
     # key width: only 4 (or 0 for 4) and 2
     bad = layout()
     bad.key_bits = 3
