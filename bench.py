@@ -72,13 +72,16 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(kernel_call):
+def measured_traffic(kernel_call, config_id, p):
     """HBM bytes per launch of a call's kernels from the committed counter summary, or None
-    when there is none or a kernel source changed since the counters were taken."""
+    when there is none, it was taken on another workload, or a kernel source changed since
+    the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
+        return None
+    if rec.get("config_id") != config_id or rec.get("p") is None or abs(rec["p"] - p) > 1e-9:
         return None
     entry = rec.get("calls", {}).get(kernel_call)
     if not entry:
@@ -507,7 +510,7 @@ def main():
     dom = max(per_stage_bytes, key=lambda k: per_stage_bytes[k])
     achieved = per_stage_bytes[dom] / (call_ms[dom] * 1e-3)
     roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK, "traffic": measured_traffic(dom), "kernel": dom,
+                "frac": achieved / HBM_PEAK, "traffic": measured_traffic(dom, args.config, p), "kernel": dom,
                 "bytes_per_launch": per_stage_bytes[dom], "avg_launch_us": call_ms[dom] * 1e3}
     step_s = graph_ms * 1e-3
     res = {
