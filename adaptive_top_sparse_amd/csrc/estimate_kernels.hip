@@ -14,6 +14,7 @@
 #include "twl_launch.h"
 
 TWL_PHASE_STORAGE(estimate)
+TWL_SPAN_STORAGE(estimate)
 
 namespace twl {
 namespace {
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   __shared__ float red_m[kEstWaves][G], red_l[kEstWaves][G];
   TWL_PHASE_BEGIN(0, 32);
   TWL_PHASE(0);
+  TWL_SPAN_BEGIN();
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -138,16 +140,21 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   const int32_t* crow = cand_pages ? cand_pages + unit * cand_stride_pages : nullptr;
 
   auto rank_of = [&](int j, int i) { return page0 + (j * kEstWaves + wave) * PB + i; };
-  // page ids of batch j, read before the candidate count is known (from inside the row).
+  // Page ids of batch j, read before the candidate count is known (from inside the row).
   // The loads are unconditional (without a page list they read page-table entry 0 and are
   // replaced by the rank), and the tests below use no short-circuit branches, so that the
-  // compiler issues a batch's loads together instead of one per branch.
+  // compiler issues a batch's loads together instead of one per branch. Page ids and
+  // page-table entries are the same for the whole wave but are loaded on the vector path
+  // (an opaque zero in the index): vector loads complete in order, so a wait for this
+  // batch's entries does not also wait for the ids already requested for the batch after
+  // next, as a wait on a scalar load would, and the pipeline below stays three deep.
   const int32_t* id_src = crow != nullptr ? crow : page_table;
+  const int vz = vgpr_zero();
   auto load_ids = [&](int j, int (&pid)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int r = rank_of(j, i);
-      const int v = id_src[crow != nullptr ? (r < page_end ? r : page0) : 0];
+      const int v = id_src[(crow != nullptr ? (r < page_end ? r : page0) : 0) + vz];
       pid[i] = crow == nullptr ? r : v;
     }
   };
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       const bool ok = (r < page_end) & (r < cnt) & (pid[i] >= 0) & (pid[i] < max_pages) &
                       (pid[i] * kPage < n);
       pid[i] = ok ? pid[i] : -1;
-      phys[i] = page_table[static_cast<long>(b) * max_pages + (ok ? pid[i] : 0)];
+      phys[i] = page_table[static_cast<long>(b) * max_pages + (ok ? pid[i] : 0) + vz];
     }
   };
   // this lane's codes (virtual group c4 of its token's row) and its group's {scale, zero}
@@ -379,6 +386,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   }
   TWL_PHASE(3);
   TWL_PHASE_FLUSH(0, 32);
+  TWL_SPAN_END();
 }
 
 // w = exp(s - M) / L with (M, L) merged from the row's chunk partials; invalid slots hold

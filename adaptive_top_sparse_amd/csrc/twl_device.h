@@ -119,11 +119,12 @@ __device__ __forceinline__ void keep_loaded(int v) { asm volatile("" ::"v"(v)); 
 // for a later load (a kernel argument, say) does not also wait for this one, as it would for
 // a scalar load, and it can be issued alongside the wave's first vector loads. The caller
 // makes the value scalar (readfirstlane) where it is needed.
-__device__ __forceinline__ int load_uniform_vec(const int32_t* p) {
+__device__ __forceinline__ int vgpr_zero() {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  return p[z];
+  return z;
 }
+__device__ __forceinline__ int load_uniform_vec(const int32_t* p) { return p[vgpr_zero()]; }
 
 __device__ __forceinline__ bool phys_ok(int phys, int num_phys) {
   return phys >= 0 && phys < num_phys;
