@@ -10,6 +10,8 @@
 // over the unit's valid candidates, done as per-chunk (max, sum of exp) partials followed
 // by a normalization pass. The logits are kept in log2 units (s_hj * log2 e), so that every
 // exponential is one exp2.
+#include <utility>
+
 #include "twl_device.h"
 #include "twl_launch.h"
 
@@ -61,13 +63,36 @@ __device__ __forceinline__ int mfma_channel(int c4, int vg_channels, int m, int 
   }
 }
 
-// Two fp16 codes from the bit fields at [3:0] and [19:16] (of which only the low BITS are
-// set): 1024 + n is exact in fp16 (its ulp is 1), so or-ing n into the significand of 1024
-// and subtracting 1024 gives n.
-__device__ __forceinline__ uint32_t codes_to_f16x2(uint32_t pair_bits) {
-  const f16x2 v = __builtin_bit_cast(f16x2, pair_bits | 0x64006400u);
-  const f16x2 r = v - f16x2{static_cast<f16>(1024.f), static_cast<f16>(1024.f)};
+// Codes K of both 16-bit halves of a code word (bits [p + BITS - 1 : p] of each half,
+// p = BITS * K) as two exact fp16 integers. A field that lies inside the fp16 significand
+// (p + BITS <= 10) is converted where it stands: with the exponent of 2^(10 - p) or-ed in,
+// the half reads 2^(10 - p) + n exactly (its ulp is 1 there), and subtracting 2^(10 - p)
+// leaves n. Higher fields are first shifted down by 8 bits, one shift that serves all of
+// them. The values are those of the plain shift-mask-convert, at fewer instructions.
+// The exponent patterns for fields at p = 0, 2, 4, 6, 8 (index p / 2), both halves. The
+// caller keeps them in VGPRs, so that mask and or go out as one v_and_or_b32 (whose one
+// scalar operand is then the mask).
+constexpr uint32_t code_exp(int p) {
+  return (static_cast<uint32_t>(25 - p) << 10) | (static_cast<uint32_t>(25 - p) << 26);
+}
+template <int BITS, int K>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t w_hi,
+                                              const uint32_t (&exp_v)[5]) {
+  constexpr uint32_t kMask = BITS == 4 ? 0x000f000fu : 0x00030003u;
+  constexpr int p0 = BITS * K;
+  constexpr bool kLow = p0 + BITS <= 10;
+  constexpr int p = kLow ? p0 : p0 - 8;
+  const uint32_t x = ((kLow ? w : w_hi) & (kMask << p)) | exp_v[p / 2];
+  const f16 off = static_cast<f16>(static_cast<float>(1 << (10 - p)));
+  const f16x2 r = __builtin_bit_cast(f16x2, x) - f16x2{off, off};
   return __builtin_bit_cast(uint32_t, r);
+}
+template <int BITS, int... K>
+__device__ __forceinline__ void code_pairs(uint32_t w, uint32_t (&bw)[16 / BITS],
+                                           const uint32_t (&exp_v)[5],
+                                           std::integer_sequence<int, K...>) {
+  const uint32_t w_hi = w >> 8;
+  ((bw[K] = code_pair<BITS, K>(w, w_hi, exp_v)), ...);
 }
 
 template <int NG>
@@ -256,6 +281,9 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   if (n_batches > 1) load_phys(1, ids1, phys1);
   TWL_PHASE(1);
 
+  uint32_t code_exp_v[5];  // code_exp(2i), held in VGPRs (vz is an opaque zero)
+#pragma unroll
+  for (int i = 0; i < 5; ++i) code_exp_v[i] = static_cast<uint32_t>(vz) + code_exp(2 * i);
   float run_m[NHB], run_l[NHB];  // online max and sum of exp of this lane's head(s)
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
@@ -278,10 +306,8 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       for (int wi = 0; wi < NW; ++wi) {
         const uint32_t w = cw0[i].w[wi];
         constexpr int kPairs = 16 / BITS;  // code pairs per word
-        constexpr uint32_t kMask = BITS == 4 ? 0x000f000fu : 0x00030003u;
         uint32_t bw[kPairs];
-#pragma unroll
-        for (int k = 0; k < kPairs; ++k) bw[k] = codes_to_f16x2((w >> (BITS * k)) & kMask);
+        code_pairs<BITS>(w, bw, code_exp_v, std::make_integer_sequence<int, kPairs>());
 #pragma unroll
         for (int m = 0; m < kPairs / 2; ++m)
           bq[wi * (kPairs / 2) + m] = __builtin_bit_cast(f16x4, u32x2{bw[2 * m], bw[2 * m + 1]});
