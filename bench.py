@@ -398,7 +398,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the hot path "
-              "is a single-GPU kernel library and this build has no multi-GPU mode.",
+              "is a single-GPU kernel library with no multi-GPU mode.",
               file=sys.stderr)
         sys.exit(2)
     import torch

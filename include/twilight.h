@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   TWL_OK = 0,
   TWL_ERR_INVALID_ARG = -1, /* null or misaligned pointer, bad size or value */
-  TWL_ERR_UNSUPPORTED = -2, /* a shape this build has no kernel for */
+  TWL_ERR_UNSUPPORTED = -2, /* a shape the library has no kernel for */
   TWL_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   TWL_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
 } twl_status_t;
