@@ -413,50 +413,6 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* ld
   return block_excl_scan<NT, uint32_t>(v, lds, total);
 }
 
-// Boundary bucket of a descending selection over 2 * NT buckets, thread t holding buckets
-// 2t and 2t+1 with weights w0, w1: the bucket b* with weight(buckets > b*) < rem <=
-// weight(buckets >= b*). Returns b*; *above = weight(buckets > b*), *in = weight(b*).
-// `lds` holds NT/64 elements, `pick` 3. Requires 0 < rem <= total weight.
-// When frac > 0, rem is replaced by max(1, ceil(frac * total weight)) and *rem_used
-// receives it, so a first pass needs no separate reduction for the total.
-template <int NT, typename T>
-__device__ __forceinline__ uint32_t block_pick_bucket(T w0, T w1, T rem, T* lds, T* pick,
-                                                      T* above, T* in, float frac = 0.f,
-                                                      T* rem_used = nullptr) {
-  constexpr int NW = NT / kWave;
-  const int t = threadIdx.x;
-  const int w = t / kWave;
-  const T incl = wave_incl_scan(static_cast<T>(w0 + w1));
-  if (lane_id() == kWave - 1) lds[w] = incl;
-  __syncthreads();
-  T x = lane_id() < NW ? lds[lane_id()] : T(0);
-  x = wave_incl_scan(x);
-  const T before = w > 0 ? readlane(x, w - 1) : T(0);
-  const T total = readlane(x, NW - 1);
-  if (frac > 0.f) {
-    rem = static_cast<T>(ceil(static_cast<double>(frac) * static_cast<double>(total)));
-    rem = rem < T(1) ? T(1) : rem;
-    if (rem_used) *rem_used = rem;
-  }
-  const T above1 = total - (before + incl);  // buckets > 2t+1
-  const T above0 = above1 + w1;              // buckets > 2t
-  if (above1 < rem && rem <= above1 + w1) {
-    pick[0] = static_cast<T>(2 * t + 1);
-    pick[1] = above1;
-    pick[2] = w1;
-  } else if (above0 < rem && rem <= above0 + w0) {
-    pick[0] = static_cast<T>(2 * t);
-    pick[1] = above0;
-    pick[2] = w0;
-  }
-  __syncthreads();
-  const uint32_t b = static_cast<uint32_t>(pick[0]);
-  *above = pick[1];
-  *in = pick[2];
-  __syncthreads();
-  return b;
-}
-
 // Boundary bucket of a descending selection over NT * BPT buckets kept in LDS. Thread t
 // owns the contiguous buckets [t*BPT, (t+1)*BPT); bucket b is stored at
 // bins[(b % BPT) * NT + b / BPT] (see bucket_slot), so that the owners' reads are
@@ -464,7 +420,10 @@ __device__ __forceinline__ uint32_t block_pick_bucket(T w0, T w1, T rem, T* lds,
 // b*); *above = weight(buckets > b*), *in = weight(b*). `lds` holds NT/64 elements, `pick`
 // 3. Requires 0 < rem <= total weight. When frac > 0, rem is replaced by
 // max(1, ceil(frac * total weight)) and *rem_used receives it, so a first pass needs no
-// separate reduction for the total.
+// separate reduction for the total. It ends without a barrier: every thread has read `lds`
+// before the second barrier and reads `pick` after it, so the caller must pass a block
+// barrier before it writes `pick` or `lds` again (the radix selections here always do, in
+// the passes between two picks).
 template <int NT, int BPT>
 __device__ __forceinline__ int bucket_slot(uint32_t b) {
   return static_cast<int>((b % BPT) * NT + b / BPT);
@@ -510,7 +469,6 @@ __device__ __forceinline__ uint32_t block_pick_bucket_lds(const T* bins, T rem, 
   const uint32_t b = static_cast<uint32_t>(pick[0]);
   *above = pick[1];
   *in = pick[2];
-  __syncthreads();
   return b;
 }
 
