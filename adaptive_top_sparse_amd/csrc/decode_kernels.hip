@@ -7,18 +7,20 @@
 //
 // Split-KV: each work-group takes a chunk of a KV head's kept list and leaves (max, sum,
 // unnormalized o) in log2 units in the workspace; a merge kernel combines the chunks and
-// writes the fp16 output. A list that fits one chunk is finished in place. Chunks are
-// small (one to four batches of rows), so that every row's chain of dependent loads is in
-// flight at once across the chip. (Merging in the
-// last work-group to finish, found with an atomic ticket, needs device-scope fences that
-// write back and invalidate whole L2s on this multi-XCD part; measured, it costs far more
-// than the second launch.)
+// writes the fp16 output. A list that fits one chunk is finished in place. Chunks are one to
+// sixteen batches of rows: short enough that every row's chain of dependent loads is in
+// flight at once across the chip when lists are short, long enough that long lists leave few
+// partials. (Merging in the last work-group to finish, found with an atomic ticket, needs
+// device-scope fences that write back and invalidate whole L2s on this multi-XCD part;
+// measured, it costs far more than the second launch.)
 //
-// Layout on the device: D/8 lanes per kept token, 8 channels (16 B of K, 16 B of V) per
-// lane, so one wave gathers 64/(D/8) token rows per load instruction, each row one
-// contiguous 2*D-byte stretch of the paged cache. q . k uses v_dot2_f32_f16 on fp16 pairs
-// (exact products, fp32 sums) reduced across the row's lanes with DPP; softmax and p * v run
-// in fp32.
+// Layout on the device: V rows (and K rows in the dot2 form) take D/8 lanes per kept token,
+// 8 channels (16 B) per lane, so one wave gathers 64/(D/8) token rows per load instruction,
+// each row one contiguous 2*D-byte stretch of the paged cache. For d = 128 and groups of
+// four or more heads, q . k runs on the matrix cores with K rows in the MFMA operand layout
+// and the weights broadcast back into the V layout; otherwise it uses v_dot2_f32_f16 on fp16
+// pairs reduced across the row's lanes with DPP. Products are exact and sums fp32 either
+// way; softmax and p * v run in fp32.
 #include "twl_device.h"
 #include "twl_launch.h"
 
