@@ -110,8 +110,8 @@ def measured_traffic(kernel_call, config_id, p):
     if not entry:
         return None
     for src, digest in entry.get("sources", {}).items():
-        p = os.path.join(ROOT, src)
-        if not os.path.exists(p) or source_digest(p) != digest:
+        path = os.path.join(ROOT, src)
+        if not os.path.exists(path) or source_digest(path) != digest:
             return None
     return entry.get("bytes_per_launch")
 
