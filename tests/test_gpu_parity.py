@@ -37,6 +37,10 @@ CASES = {
 }
 
 
+# the cases whose workload has a Quest page selector (the others build no page bounds)
+QUEST_CASES = [k for k, (cfg, *_) in CASES.items() if workloads.SPECS[cfg].base is not None]
+
+
 def _run(w, p, repeat=1, key_bits=4):
     """Run i uses the separate estimate and top-p calls (so that the normalised weights
     can be checked) when i is even, the single fused call when i is odd."""
@@ -84,10 +88,10 @@ def test_quantized_keys_bit_exact(case):
         assert np.array_equal(meta[..., 1].astype(np.float64), res["zero"].astype(np.float64))
 
 
+@pytest.mark.parametrize("case", QUEST_CASES, indirect=True)
 def test_page_bounds_bit_exact(case):
     w, host, orc = case["w"], case["host"], case["orc"]
-    if host["page_minmax"] is None:
-        pytest.skip("no page selector in this workload")
+    assert host["page_minmax"] is not None
     for (b, g), res in orc.items():
         n = int(w.seq_lens[b])
         P = -(-n // 16)
@@ -96,10 +100,10 @@ def test_page_bounds_bit_exact(case):
         assert np.array_equal(mm[:, 1].astype(np.float64), res["hi"].astype(np.float64)), (b, g)
 
 
+@pytest.mark.parametrize("case", QUEST_CASES, indirect=True)
 def test_quest_pages_bit_exact(case):
     w, out, orc = case["w"], case["out"], case["orc"]
-    if out["sel_pages"] is None:
-        pytest.skip("no page selector in this workload")
+    assert out["sel_pages"] is not None
     for (b, g), res in orc.items():
         cnt = int(out["sel_count"][b, g])
         assert cnt == len(res["sel"]), (b, g)
