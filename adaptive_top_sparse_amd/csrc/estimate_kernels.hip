@@ -95,23 +95,34 @@ __device__ __forceinline__ void code_pairs(uint32_t w, uint32_t (&bw)[16 / BITS]
   ((bw[K] = code_pair<BITS, K>(w, w_hi, exp_v)), ...);
 }
 
+// *(p + off bytes) with p wave-uniform and off a 32-bit vector offset: the load takes the
+// global_load form with a scalar base, so a wave-uniform address costs no 64-bit vector
+// arithmetic, and it stays a vector-memory load (completed in order). The offset gets a
+// fresh opaque zero added at each call, so that the compiler cannot hoist a vector copy of
+// p + off out of a loop and form the addresses from it.
+template <typename T>
+__device__ __forceinline__ T load_at(const T* p, uint32_t off) {
+  const uint32_t o = off + static_cast<uint32_t>(vgpr_zero());
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + o);
+}
+
 template <int NG>
 struct CodeWords {
   uint32_t w[NG];
 };
 template <int NG>
-__device__ __forceinline__ CodeWords<NG> load_words(const uint32_t* p) {
+__device__ __forceinline__ CodeWords<NG> load_words(const uint32_t* p, uint32_t off) {
   CodeWords<NG> r;
   if constexpr (NG == 4) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 v = load_at(reinterpret_cast<const u32x4*>(p), off);
     r.w[0] = v[0];
     r.w[1] = v[1];
     r.w[2] = v[2];
     r.w[3] = v[3];
   } else if constexpr (NG == 1) {
-    r.w[0] = *p;
+    r.w[0] = load_at(p, off);
   } else {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 v = load_at(reinterpret_cast<const u32x2*>(p), off);
     r.w[0] = v[0];
     r.w[1] = v[1];
   }
@@ -173,13 +184,15 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   // (an opaque zero in the index): vector loads complete in order, so a wait for this
   // batch's entries does not also wait for the ids already requested for the batch after
   // next, as a wait on a scalar load would, and the pipeline below stays three deep.
+  // Once such a value has arrived it is made scalar (readfirstlane), so that the checks and
+  // address arithmetic that follow run on the scalar unit.
   const int32_t* id_src = crow != nullptr ? crow : page_table;
   const int vz = vgpr_zero();
   auto load_ids = [&](int j, int (&pid)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int r = rank_of(j, i);
-      const int v = id_src[(crow != nullptr ? (r < page_end ? r : page0) : 0) + vz];
+      const int v = load_at(id_src + (crow != nullptr ? (r < page_end ? r : page0) : 0), 0u);
       pid[i] = crow == nullptr ? r : v;
     }
   };
@@ -193,26 +206,34 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
                                         (cand_count != nullptr ? unit : 0));
   int cnt = cand_stride_pages;  // set after the q staging
   // validated page ids and their page-table entries
+  const int32_t* pt_row = page_table + static_cast<long>(b) * max_pages;
   auto load_phys = [&](int j, int (&pid)[PB], int (&phys)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int r = rank_of(j, i);
-      const bool ok = (r < page_end) & (r < cnt) & (pid[i] >= 0) & (pid[i] < max_pages) &
-                      (pid[i] * kPage < n);
-      pid[i] = ok ? pid[i] : -1;
-      phys[i] = page_table[static_cast<long>(b) * max_pages + (ok ? pid[i] : 0) + vz];
+      const int ps = __builtin_amdgcn_readfirstlane(pid[i]);
+      const bool ok = (r < page_end) & (r < cnt) & (ps >= 0) & (ps < max_pages) &
+                      (ps * kPage < n);
+      pid[i] = ok ? ps : -1;
+      phys[i] = load_at(pt_row + (ok ? ps : 0), 0u);
     }
   };
-  // this lane's codes (virtual group c4 of its token's row) and its group's {scale, zero}
+  // this lane's codes (virtual group c4 of its token's row) and its group's {scale, zero}:
+  // the page's first row is a scalar base, the lane's part a small byte offset
+  const uint32_t code_off = static_cast<uint32_t>(tok_in_page * RB + c4 * NW * 4);
+  const uint32_t meta_off = static_cast<uint32_t>((tok_in_page * NG + c4 * VG / 32) * 4);
   auto load_codes = [&](int (&pid)[PB], const int (&phys)[PB], CodeWords<NW> (&cw)[PB],
                         uint32_t (&mw)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const bool ok = (pid[i] >= 0) & (phys[i] >= 0) & (phys[i] < num_phys);
-      pid[i] = ok ? pid[i] : -1;
-      const long row = ok ? (static_cast<long>(phys[i]) * Hkv + g) * kPage + tok_in_page : 0;
-      cw[i] = load_words<NW>(reinterpret_cast<const uint32_t*>(codes + row * RB) + c4 * NW);
-      mw[i] = meta[row * NG + c4 * VG / 32];
+      const int phs = __builtin_amdgcn_readfirstlane(phys[i]);
+      const int pis = __builtin_amdgcn_readfirstlane(pid[i]);
+      const bool ok = (pis >= 0) & (phs >= 0) & (phs < num_phys);
+      pid[i] = ok ? pis : -1;
+      // rows of an invalid page read page 0 of head 0 (always present) and are discarded
+      const long row0 = ok ? (static_cast<long>(phs) * Hkv + g) * kPage : 0;
+      cw[i] = load_words<NW>(reinterpret_cast<const uint32_t*>(codes + row0 * RB), code_off);
+      mw[i] = load_at(meta + row0 * NG, meta_off);
     }
   };
   // the group's queries and their per-group sums, staged while the first ids are in flight:
@@ -314,35 +335,21 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       }
       const float scale = h2f(static_cast<uint16_t>(mw0[i] & 0xffffu));
       const float zero = h2f(static_cast<uint16_t>(mw0[i] >> 16));
-      const int t = ids0[i] * kPage + tok_in_page;
-      const bool valid = ids0[i] >= 0 && t < n;
+      const bool valid = (ids0[i] >= 0) & (tok_in_page < n - ids0[i] * kPage);
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < MPT; ++m)
           d = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[hb][m], bq[m], d, 0, 0, 0);
-        // this lane group's term for heads r + 4 hb, summed over the four lane groups
-        float tot[4];
+        // this lane group's terms for heads r + 4 hb, summed over the four lane groups so
+        // that lane group c4 ends with head c4 + 4 hb (a reduce-scatter: each swap moves two
+        // different values, and no lane forms a total it does not keep)
+        float v[4], tot[1];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = fmaf(scale, d[r], zero * qg[hb][r]);
-          {
-            const auto x = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v),
-                                                            __builtin_bit_cast(int, v), false, false);
-            v = __builtin_bit_cast(float, static_cast<int>(x[0])) +
-                __builtin_bit_cast(float, static_cast<int>(x[1]));
-          }
-          {
-            const auto x = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v),
-                                                            __builtin_bit_cast(int, v), false, false);
-            v = __builtin_bit_cast(float, static_cast<int>(x[0])) +
-                __builtin_bit_cast(float, static_cast<int>(x[1]));
-          }
-          tot[r] = v;
-        }
-        // lane group c4 keeps head c4 + 4 hb
-        const float mine = c4 == 0 ? tot[0] : c4 == 1 ? tot[1] : c4 == 2 ? tot[2] : tot[3];
+        for (int r = 0; r < 4; ++r) v[r] = fmaf(scale, d[r], zero * qg[hb][r]);
+        sum_rows_scatter<4>(v, tot);
+        const float mine = tot[0];
         s[i][hb] = (valid && c4 + 4 * hb < G) ? scale_log2 * mine : -INFINITY;
       }
       // logits row entries (every slot of the chunk is written, -inf when not a candidate)
