@@ -426,6 +426,17 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       hi = nhi;
       TWL_PHASE(4 + (pass_no < 4 ? pass_no : 4));
       if (shift == 0) break;
+      {
+        // No key of the bucket has a mass above fixed_mass(hi), so it holds at least
+        // inb / fixed_mass(hi) keys; when that bound exceeds 64 the collection below would
+        // come back too long, so the next pass starts at once. (fp64: inb < 2^57 rounds by
+        // at most one part in 2^53, and 64.5 * mh is exact, so the test implies > 64 keys.)
+        const uint64_t mh = fixed_mass(hi, e);
+        if (mh != 0 && static_cast<double>(inb) > 64.5 * static_cast<double>(mh)) {
+          ++pass_no;
+          continue;
+        }
+      }
       // Short boundary bucket: collect its keys and let one wave finish the search.
       // tau is then the largest key whose mass together with every larger key of the
       // bucket reaches rem (0 < rem <= the bucket's mass, so one exists).
