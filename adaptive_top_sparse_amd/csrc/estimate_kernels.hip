@@ -181,13 +181,12 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   // replaced by the rank), and the tests below use no short-circuit branches, so that the
   // compiler issues a batch's loads together instead of one per branch. Page ids and
   // page-table entries are the same for the whole wave but are loaded on the vector path
-  // (an opaque zero in the index): vector loads complete in order, so a wait for this
+  // (load_at, an opaque zero in the offset): vector loads complete in order, so a wait for this
   // batch's entries does not also wait for the ids already requested for the batch after
   // next, as a wait on a scalar load would, and the pipeline below stays three deep.
   // Once such a value has arrived it is made scalar (readfirstlane), so that the checks and
   // address arithmetic that follow run on the scalar unit.
   const int32_t* id_src = crow != nullptr ? crow : page_table;
-  const int vz = vgpr_zero();
   auto load_ids = [&](int j, int (&pid)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
@@ -303,6 +302,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   TWL_PHASE(1);
 
   uint32_t code_exp_v[5];  // code_exp(2i), held in VGPRs (vz is an opaque zero)
+  const int vz = vgpr_zero();
 #pragma unroll
   for (int i = 0; i < 5; ++i) code_exp_v[i] = static_cast<uint32_t>(vz) + code_exp(2 * i);
   float run_m[NHB], run_l[NHB];  // online max and sum of exp of this lane's head(s)
