@@ -1,6 +1,7 @@
 """GPU edge cases of the hot path, through the C ABI: empty and tiny sequences, budgets
 that cover every page, p = 1, a single kept token, exact Quest ties, graph replay,
-appending one token, and host-side errors that must leave the outputs untouched."""
+appending one token, a top-p boundary among thousands of equal or near-equal weights, and
+host-side errors that must leave the outputs untouched."""
 import numpy as np
 import pytest
 
@@ -377,3 +378,54 @@ def test_append_keys_tie_rules_match_oracle(d, bits):
                 assert np.array_equal(mm_h[b, kvh, page, 0], lo[page].view(np.uint16)), (b, kvh, page)
                 assert np.array_equal(mm_h[b, kvh, page, 1], hi[page].view(np.uint16)), (b, kvh, page)
                 assert np.array_equal(mm_h[b, kvh, page], full[2][b, kvh, page])
+
+
+@pytest.mark.parametrize("kind", ["ties", "narrow"])
+def test_topp_boundary_bucket_of_thousands_of_keys(kind):
+    """Crafted weights whose top-p boundary falls among 20000 keys packed into a sliver of
+    one binade, so that the first histogram passes land on a boundary bucket of thousands
+    of keys (which the kernel passes over without collecting them) before the search ends:
+    on exact ties, or among keys within 1/128 of each other. tau equals the oracle's on the
+    same weights; the kept set is exactly the threshold set {W >= tau}, which holds the
+    oracle's minimal nucleus and differs from it only by weights equal to tau."""
+    pl = _pipeline()
+    print(f"\n[edge] top-p boundary bucket of thousands of keys: {kind}", flush=True)
+    n = 40960
+    w = workloads.make_workload(5, B=1, n=n, Hq=1, Hkv=1)
+    c = pl.upload(w)
+    c.build_caches()
+    buf = pl.alloc_step(c)
+    rng = np.random.default_rng(7)
+    W = np.zeros(n, np.float32)
+    slots = rng.permutation(n)
+    big, mid = slots[:1000], slots[1000:21000]
+    W[big] = rng.uniform(1e-4, 5e-4, big.size).astype(np.float32)
+    w0 = np.float32(2.0 ** -16)
+    if kind == "ties":
+        W[mid] = w0
+    else:
+        W[mid] = (w0 * (1.0 + rng.uniform(0.0, 2.0 ** -7, mid.size))).astype(np.float32)
+    rest = slots[21000:]
+    W[rest] = np.exp(rng.uniform(np.log(1e-9), np.log(1e-6), rest.size)).astype(np.float32)
+    stride = c.cand_stride_pages
+    weights = torch.zeros((1, 1, stride * 16), dtype=torch.float32, device="cuda")
+    weights[0, 0, :n] = torch.from_numpy(W).cuda()
+    p = 0.9
+    lay = c.layout()
+    twl.twilight_topp_select(lay, weights, None, None, stride, p, buf.kept, buf.kept_count,
+                             buf.tau, buf.workspace)
+    torch.cuda.synchronize()
+    kc = int(buf.kept_count[0, 0])
+    kept = buf.kept[0, 0, :kc].cpu().numpy()
+    tau = float(buf.tau[0, 0])
+    valid = np.zeros(stride * 16, bool)
+    valid[:n] = True
+    o_kept, o_tau = oracle.topp_select(weights[0].cpu().numpy().astype(np.float64), valid, p)
+    # the boundary lies among the packed keys: the big weights alone fall short of p
+    assert W[big].astype(np.float64).sum() < p * W.astype(np.float64).sum()
+    assert w0 <= o_tau <= w0 * (1.0 + 2.0 ** -7)
+    assert tau == o_tau
+    assert np.array_equal(kept, np.flatnonzero((W > 0) & (W >= np.float32(tau))))
+    extra = np.setdiff1d(kept, o_kept)
+    assert np.setdiff1d(o_kept, kept).size == 0
+    assert np.all(W[extra] == np.float32(tau))
