@@ -1,7 +1,8 @@
 """GPU edge cases of the hot path, through the C ABI: empty and tiny sequences, budgets
 that cover every page, p = 1, a single kept token, exact Quest ties, graph replay,
-appending one token, a top-p boundary among thousands of equal or near-equal weights, and
-host-side errors that must leave the outputs untouched."""
+appending one token, a top-p boundary among thousands of equal or near-equal weights,
+invalid candidate ids and page-table entries, and host-side errors that must leave the
+outputs untouched."""
 import numpy as np
 import pytest
 
@@ -429,3 +430,59 @@ def test_topp_boundary_bucket_of_thousands_of_keys(kind):
     extra = np.setdiff1d(kept, o_kept)
     assert np.setdiff1d(o_kept, kept).size == 0
     assert np.all(W[extra] == np.float32(tau))
+
+
+def test_estimate_skips_invalid_candidates_and_page_entries():
+    """Candidate lists with ids below 0, at or past max_pages and past the sequence, and
+    page-table entries below 0 or past num_phys_pages: every such page is skipped as if
+    absent (its slots exactly 0, outside the softmax), and the other slots match the
+    oracle's estimate over the same list with those pages marked absent."""
+    pl = _pipeline()
+    print("\n[edge] estimate with invalid candidate ids and page entries", flush=True)
+    w = workloads.make_workload(3, n=2048 + 5, budget=32)
+    c = pl.upload(w)
+    c.build_caches()
+    buf = pl.alloc_step(c)
+    pl.run_step(c, buf, 0.9, stages=("select",))
+    torch.cuda.synchronize()
+    s, G, B, Hkv = w.spec, w.spec.G, len(w.seq_lens), w.spec.Hkv
+    P = -(-int(w.seq_lens[0]) // 16)
+    cand = buf.sel_pages.cpu().numpy().copy()
+    cnt = buf.sel_count.cpu().numpy()
+    assert np.all(cnt == 32)
+    # still ascending: an id below 0 first, then one page past the sequence and two ids at
+    # or past max_pages last
+    cand[:, :, 0] = -5
+    cand[:, :, 29] = P
+    cand[:, :, 30] = c.max_pages + 3
+    cand[:, :, 31] = c.max_pages + 10
+    torn = {int(cand[0, 0, 15]): -1, int(cand[0, 0, 20]): c.num_phys + 7}
+    pt = c.page_table.clone()
+    for lp, bad in torn.items():
+        c.page_table[0, lp] = bad
+    lay = c.layout()
+    stride = c.cand_stride_pages
+    weights = torch.full((B, s.Hq, stride * 16), 7.0, dtype=torch.float32, device="cuda")
+    twl.twilight_estimate_weights(lay, c.q, c.k_codes, c.k_meta,
+                                  torch.from_numpy(cand).cuda(), buf.sel_count, stride,
+                                  parity.sm_scale_for(s.d), weights, buf.workspace)
+    torch.cuda.synchronize()
+    c.page_table.copy_(pt)
+    got = weights.cpu().numpy()
+    sm = parity.sm_scale_for(s.d)
+    for b in range(B):
+        n = int(w.seq_lens[b])
+        for g in range(Hkv):
+            lst = cand[b, g, :int(cnt[b, g])].astype(np.int64)
+            lst = np.where(np.isin(lst, list(torn)) & (b == 0), -1, lst)
+            codes, scale, zero = oracle.quantize_keys(w.k[b][g][:n])
+            ref = oracle.estimate_weights(w.q[b, g * G:(g + 1) * G], codes, scale, zero, n,
+                                          lst.astype(np.int32), stride * 16, sm)
+            pages = np.repeat(lst, 16)
+            toks = pages * 16 + np.tile(np.arange(16), lst.size)
+            valid = np.zeros(stride * 16, bool)
+            valid[:toks.size] = (pages >= 0) & (toks < n)
+            assert not valid[:16].any() and not valid[29 * 16:].any()
+            assert np.array_equal(valid, ref.sum(axis=0) > 0)
+            parity.check_weights(got[b, g * G:(g + 1) * G], ref, valid)
+            np.testing.assert_allclose(got[b, g * G:(g + 1) * G].sum(axis=1), 1.0, rtol=1e-5)
