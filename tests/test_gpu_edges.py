@@ -1,8 +1,8 @@
 """GPU edge cases of the hot path, through the C ABI: empty and tiny sequences, budgets
 that cover every page, p = 1, a single kept token, exact Quest ties, graph replay,
 appending one token, a top-p boundary among thousands of equal or near-equal weights,
-invalid candidate ids and page-table entries, and host-side errors that must leave the
-outputs untouched."""
+invalid candidate ids, kept ids and page-table entries, and host-side errors that must
+leave the outputs untouched."""
 import numpy as np
 import pytest
 
@@ -486,3 +486,48 @@ def test_estimate_skips_invalid_candidates_and_page_entries():
             assert np.array_equal(valid, ref.sum(axis=0) > 0)
             parity.check_weights(got[b, g * G:(g + 1) * G], ref, valid)
             np.testing.assert_allclose(got[b, g * G:(g + 1) * G].sum(axis=1), 1.0, rtol=1e-5)
+
+
+def test_decode_skips_invalid_kept_ids_and_page_entries():
+    """Kept lists holding ids below 0 and at or past seq_len, and kept tokens whose page
+    entry is below 0 or past num_phys_pages: each such entry is skipped as if absent, and
+    the output is the oracle's attention over the remaining tokens."""
+    pl = _pipeline()
+    print("\n[edge] decode with invalid kept ids and page entries", flush=True)
+    w = workloads.make_workload(3, n=3000 + 7, budget=64)
+    c = pl.upload(w)
+    c.build_caches()
+    buf = pl.alloc_step(c)
+    s, G, Hkv = w.spec, w.spec.G, w.spec.Hkv
+    n = int(w.seq_lens[0])
+    stride = buf.kept.shape[2]
+    rng = np.random.default_rng(11)
+    kept = np.full((1, Hkv, stride), -1, np.int32)
+    counts = np.zeros((1, Hkv), np.int32)
+    torn_pages = {3: -1, 40: c.num_phys + 5}
+    valid_lists = []
+    for g in range(Hkv):
+        ids = np.sort(rng.choice(n, size=500, replace=False)).astype(np.int32)
+        ids[:3] = np.sort(rng.choice(16, size=3, replace=False)) + 3 * 16   # page 3 (torn)
+        ids[3:6] = np.sort(rng.choice(16, size=3, replace=False)) + 40 * 16  # page 40 (torn)
+        ids = np.unique(ids)
+        lst = np.concatenate([[-3], ids, [n, n + 100]]).astype(np.int32)
+        kept[0, g, :lst.size] = lst
+        counts[0, g] = lst.size
+        valid_lists.append(ids[~np.isin(ids // 16, list(torn_pages))])
+    pt = c.page_table.clone()
+    for lp, bad in torn_pages.items():
+        c.page_table[0, lp] = bad
+    out = torch.full((1, s.Hq, s.d), 9.0, dtype=torch.float16, device="cuda")
+    sm = parity.sm_scale_for(s.d)
+    twl.twilight_sparse_decode(c.layout(), c.q, c.k_cache, c.v_cache,
+                               torch.from_numpy(kept).cuda(), torch.from_numpy(counts).cuda(),
+                               stride, sm, out, buf.workspace)
+    torch.cuda.synchronize()
+    c.page_table.copy_(pt)
+    got = out.cpu().numpy().astype(np.float64)
+    for g in range(Hkv):
+        ref = oracle.sparse_attention(w.q[0, g * G:(g + 1) * G], w.k[0][g], w.v[0][g],
+                                      valid_lists[g], sm)
+        err = float(np.abs(got[0, g * G:(g + 1) * G] - ref).max())
+        assert err <= parity.OUT_ATOL, f"kv head {g}: err {err:.3e}"
