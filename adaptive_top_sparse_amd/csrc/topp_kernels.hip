@@ -26,20 +26,12 @@
 #include "twl_device.h"
 #include "twl_launch.h"
 
-TWL_PHASE_STORAGE(topp)
-
 namespace twl {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBins = 2048;
-// Units up to this many slots use 256-thread blocks (a tuning option, off by default: with
-// one wave per SIMD the longer per-lane code is slower than four waves sharing a SIMD).
-#ifndef TWL_TOPP_SMALL_UNIT
-#define TWL_TOPP_SMALL_UNIT 0
-#endif
-constexpr int kSmallUnit = TWL_TOPP_SMALL_UNIT;
 constexpr int kMeanThreads = 256;
 constexpr int kMeanSlots = kMeanThreads * 16;  // slots per work-group of the group-mean pass
 
@@ -223,8 +215,6 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   __shared__ uint64_t pick[3];
   __shared__ uint32_t n_short[2], short_keys[kWave + 1];
   __shared__ float s_norm[2][G];
-  TWL_PHASE_BEGIN(0, 32);
-  TWL_PHASE(0);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
   const long unit = static_cast<long>(b) * units + g;
@@ -315,10 +305,13 @@ __global__ __launch_bounds__(NT) void topp_kernel(
         float acc = 0.f;
 #pragma unroll
         for (int h = 0; h < G; ++h) acc += x[i][h][j];
-        const float w = (t0 >= 0 && t0 + j < n) ? fmaxf(acc * inv_g, 0.f) : 0.f;
+        // a slot off the candidates holds -1 (never kept); a candidate holds its mean
+        // weight, +0 when that is not positive (so p = 1 can keep it all the same)
+        const float mw = acc * inv_g;
+        const float w = (t0 >= 0 && t0 + j < n) ? (mw > 0.f ? mw : 0.f) : -1.0f;
         dst[i][j] = w;
         const uint32_t k = __float_as_uint(w);
-        if (k > 0) {
+        if (w > 0.f) {
           kmax = k > kmax ? k : kmax;
           kmin = k < kmin ? k : kmin;
         }
@@ -356,9 +349,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     if (NL == 0 && v == 0) resolve_counts();
     finish_batch(v, x, pid, W + v, kKeepT0 ? T0 + v : nullptr);
   }
-  TWL_PHASE(1);
   block_minmax<NT, uint32_t>(kmin, kmax, red_a, red_b, 0xffffffffu, 0u, &kmin, &kmax);
-  TWL_PHASE(2);
 
   // f(v, w) for every vector v of this lane's resident W, in vector order
   auto for_each_w = [&](auto&& f) {
@@ -376,13 +367,15 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     }
   };
 
+  // p = 1 keeps every candidate, whatever its weight (an fp32 weight may underflow to 0);
+  // otherwise the kept set is {W >= tau} with tau > 0
+  const bool keep_all = p >= 1.0f;
   float tau = 0.f;
-  if (kmax != 0 && p >= 1.0f) {
-    tau = __uint_as_float(kmin);
+  if (keep_all) {
+    tau = kmax != 0 ? __uint_as_float(kmin) : 0.f;
   } else if (kmax != 0) {
     // fixed-point masses relative to the largest weight's binade
     const int e = static_cast<int>((kmax >> 23) & 0xff) - 127;
-    TWL_PHASE(3);
     // the first pass covers every positive W, so its scan yields the total mass and the
     // target ceil(p * total)
     uint64_t rem = 0;
@@ -398,7 +391,6 @@ __global__ __launch_bounds__(NT) void topp_kernel(
         if (threadIdx.x == 0) n_short[pass_no & 1] = 0u;
         __syncthreads();
       }
-      if (pass_no == 0) TWL_PHASE(12);
       for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll
         for (int j = 0; j < VW; ++j) {
@@ -412,9 +404,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
         // atomics (which would need two VGPRs per slot)
         __builtin_amdgcn_sched_barrier(0);
       });
-      if (pass_no == 0) TWL_PHASE(13);
       __syncthreads();
-      if (pass_no == 0) TWL_PHASE(14);
       uint64_t above, inb;
       const uint32_t bucket = block_pick_bucket_lds<NT, BPT, uint64_t>(
           mass, rem, red64, pick, &above, &inb, pass_no == 0 ? p : 0.f, &rem);
@@ -424,7 +414,6 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       const uint32_t nhi = (hi - nlo) < span ? hi : nlo + span;
       lo = nlo;
       hi = nhi;
-      TWL_PHASE(4 + (pass_no < 4 ? pass_no : 4));
       if (shift == 0) break;
       {
         // No key of the bucket has a mass above fixed_mass(hi), so it holds at least
@@ -451,9 +440,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
           }
         }
       });
-      if (pass_no == 0) TWL_PHASE(15);
       __syncthreads();
-      if (pass_no == 0) TWL_PHASE(16);
       const uint32_t n_in = __builtin_amdgcn_readfirstlane(n_short[par]);
       ++pass_no;
       if (n_in > kWave) continue;
@@ -472,7 +459,6 @@ __global__ __launch_bounds__(NT) void topp_kernel(
           s_part += (j < static_cast<int>(n_in) && kj >= my_key) ? fixed_mass(kj, e) : 0ull;
         }
         part[wv * kWave + lane] = s_part;
-        TWL_PHASE(17);
         __syncthreads();
         if (wv == 0) {
           uint64_t s_ge = 0;  // mass of the bucket's keys >= my_key
@@ -484,19 +470,18 @@ __global__ __launch_bounds__(NT) void topp_kernel(
         }
       }
       __syncthreads();
-      TWL_PHASE(18);
       lo = short_keys[kWave];
       break;
     }
     tau = __uint_as_float(lo);
   }
 
-  TWL_PHASE(9);
   // compaction in slot order: wave totals first, then per-vector wave scans
+  auto kept_w = [&](float w) { return keep_all ? w >= 0.f : (w > 0.f && w >= tau); };
   uint32_t nk = 0;
   for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll
-    for (int j = 0; j < VW; ++j) nk += (w[j] > 0.f && w[j] >= tau) ? 1u : 0u;
+    for (int j = 0; j < VW; ++j) nk += kept_w(w[j]) ? 1u : 0u;
   });
   nk = wave_reduce(nk, OpSum());
   if (lane == 0) wave_tot[wv] = nk;
@@ -508,13 +493,12 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     run += i < wv ? c : 0u;
     total += c;
   }
-  TWL_PHASE(10);
   int32_t* out = kept + unit * n_slots;
   // register vectors reuse the tokens found while forming W; LDS vectors look them up
   auto emit = [&](int v, const float(&w)[VW], int t0_known) {
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < VW; ++j) c += (w[j] > 0.f && w[j] >= tau) ? 1u : 0u;
+    for (int j = 0; j < VW; ++j) c += kept_w(w[j]) ? 1u : 0u;
     const uint32_t incl = wave_incl_scan(c);
     if (c != 0) {
       const int s0 = wbase + v * kWave * VW + lane * VW;
@@ -525,7 +509,7 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       uint32_t pos = run + incl - c;
 #pragma unroll
       for (int j = 0; j < VW; ++j)
-        if (w[j] > 0.f && w[j] >= tau) out[pos++] = t0 + j;
+        if (kept_w(w[j])) out[pos++] = t0 + j;
     }
     run += readlane(incl, kWave - 1);
   };
@@ -545,8 +529,6 @@ __global__ __launch_bounds__(NT) void topp_kernel(
     kept_count[unit] = static_cast<int32_t>(total);
     if (tau_out) tau_out[unit] = tau;
   }
-  TWL_PHASE(11);
-  TWL_PHASE_FLUSH(0, 32);
 }
 
 // Everything a launch needs besides the kernel's template arguments.
@@ -584,7 +566,7 @@ void launch_mean(const ToppArgs& a) {
                                                       a.norm_chunks);
 }
 
-int block_threads(int n_slots) { return n_slots <= kSmallUnit ? 256 : 1024; }
+int block_threads(int) { return 1024; }
 
 int slots_per_thread(int n_slots) {
   const int nt = block_threads(n_slots);
@@ -640,19 +622,6 @@ hipError_t launch_topp(const Layout& L, const float* weights, const int32_t* can
                                             stage_offset),
                    s, norm, norm_chunks};
   const int n_slots = cand_stride_pages * kPage;
-#if TWL_TOPP_SMALL_UNIT > 0
-  if (block_threads(n_slots) == 256) {
-    switch (slots_per_thread(n_slots)) {
-      case 1: launch_spt<256, 1>(a); break;
-      case 2: launch_spt<256, 2>(a); break;
-      case 4: launch_spt<256, 4>(a); break;
-      case 8: launch_spt<256, 8>(a); break;
-      case 16: launch_spt<256, 16>(a); break;
-      default: launch_spt<256, 32>(a); break;
-    }
-    return hipGetLastError();
-  }
-#endif
   switch (slots_per_thread(n_slots)) {
     case 1: launch_spt<1024, 1>(a); break;
     case 2: launch_spt<1024, 2>(a); break;

@@ -149,7 +149,12 @@ int quest_top_pages(const twl_layout_t* L, const double* scores, int32_t budget_
  * seq_len_b. With cand_pages == NULL every page is a candidate (slot j is token j; then
  * cand_stride_pages must be >= max_pages_per_seq). For each query head h:
  * s_hj = sm_scale * q_h . dequant(k_j); weights = softmax of s_h over the valid slots;
- * invalid slots get exactly 0.
+ * invalid slots get exactly 0. Weights are fp32 and carry full precision down to 2^-126,
+ * the bottom of fp32's normal range: a weight whose exact value is below 2^-126 (a logit
+ * more than about 87 nats below its head's largest) comes out as some value in
+ * [0, 2^-126), 0 included, since the exponentials run on the transcendental unit, which
+ * returns 0 for results below the normal range. Top-p does not depend on such weights
+ * beyond its mass tolerance, and at p = 1 it keeps their tokens all the same.
  *   cand_pages : int32 [B, Hkv, cand_stride_pages] ascending page ids, or NULL
  *   cand_count : int32 [B, Hkv], or NULL (then min(P_b, cand_stride_pages))
  *   weights    : fp32 [B, Hq, cand_stride_pages * 16] */
@@ -164,11 +169,11 @@ int twilight_estimate_weights(const twl_layout_t* L, const void* q, const uint8_
  * group). W_j = mean over the group's G heads of weights[h, j] on the valid slots. tau is
  * the largest threshold whose kept mass sum_{W_j >= tau} W_j reaches p * sum_j W_j
  * (masses summed exactly in fixed point, in units of 2^-40 of the largest W's binade);
- * p == 1 keeps every slot with W > 0. The kept slots are compacted into ascending logical
- * token ids.
+ * p == 1 prunes nothing: every valid slot is kept, whatever its W (0 included). The kept
+ * slots are compacted into ascending logical token ids.
  *   kept       : int32 [B, Hkv, cand_stride_pages * 16] (entries past kept_count untouched)
  *   kept_count : int32 [B, Hkv]
- *   tau        : fp32 [B, Hkv] or NULL
+ *   tau        : fp32 [B, Hkv] or NULL; at p == 1 the smallest positive W (0 if none)
  * Supports cand_stride_pages * 16 <= 65536 slots per unit. */
 int twilight_topp_select(const twl_layout_t* L, const float* weights,
                          const int32_t* cand_pages, const int32_t* cand_count,

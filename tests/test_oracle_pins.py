@@ -354,7 +354,7 @@ def test_topp_special_cases():
     assert list(kept) == list(range(30))
     onehot = np.zeros(30)
     onehot[17] = 1.0
-    for p in (1e-6, 0.5, 0.9, 1.0):
+    for p in (1e-6, 0.5, 0.9, float(np.float32(1.0 - 2.0 ** -24))):
         kept, tau = oracle.topp_select(onehot[None], ones, p)
         assert list(kept) == [17]
         assert tau == 1.0
@@ -372,11 +372,16 @@ def test_topp_mass_exactly_at_target_stops_there():
     assert m_star == 2
 
 
-def test_topp_one_hot_at_p_one_keeps_only_positive_weights():
+def test_topp_at_p_one_keeps_every_valid_slot_even_zero_weights():
+    # p = 1 prunes nothing: a one-hot distribution keeps all its valid slots (weights that
+    # are 0, e.g. underflowed, included), and invalid slots stay out
     onehot = np.zeros(30)
     onehot[17] = 1.0
-    kept, _ = oracle.topp_select(onehot[None], np.ones(30, bool), 1.0)
-    assert list(kept) == [17]
+    valid = np.ones(30, bool)
+    valid[25:] = False
+    kept, tau = oracle.topp_select(onehot[None], valid, 1.0)
+    assert list(kept) == list(range(25))
+    assert tau == 0.0
 
 
 def test_topp_group_mean_equals_single_head_on_the_mean():
