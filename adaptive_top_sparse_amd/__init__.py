@@ -13,9 +13,7 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# TWILIGHT_LIB may name another build of the same library (for example one compiled with
-# different tuning constants); by default the in-tree build is used.
-LIB_PATH = os.environ.get("TWILIGHT_LIB") or os.path.join(HERE, "libtwilight.so")
+LIB_PATH = os.path.join(HERE, "libtwilight.so")
 PAGE_SIZE = 16
 
 TWL_OK = 0

@@ -24,9 +24,6 @@
 #include "twl_device.h"
 #include "twl_launch.h"
 
-TWL_PHASE_STORAGE(decode)
-TWL_SPAN_STORAGE(decode)
-
 namespace twl {
 namespace {
 
@@ -94,9 +91,6 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   constexpr int kRedQ = (G * 9 + 3) / 4;
   __shared__ float s_m[kDecWaves][G];
   __shared__ float s_red[kDecWaves][4 * kRedQ][LPT + 1];
-  TWL_PHASE_BEGIN(0, 32);
-  TWL_PHASE(0);
-  TWL_SPAN_BEGIN();
 
   // work-groups are numbered chunk-major (every KV head's first chunk, then every second
   // chunk, ...), so that chunks past a short kept list, which exit at once, are dispatched
@@ -192,7 +186,6 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   // them past the branches, behind a wait on every load in flight)
 #pragma unroll
   for (int u = 0; u < NU; ++u) keep_loaded(phys0[u]);
-  TWL_PHASE(4);
 
   K = K < 0 ? 0 : (K > kept_stride ? kept_stride : K);
   if (K == 0) {
@@ -250,7 +243,6 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   bool live0[U];
   u32x4 kx0[KX], vv0[U];
   load_kv(phys0, tok0, live0, kx0, vv0);
-  TWL_PHASE(5);
   if constexpr (!kSingle) {
     if (n_batches > 1) load_rows(1, t1, ids1, phys1, tok1);
   }
@@ -333,7 +325,6 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
         m[h] = mn;
       }
     }
-    if (j == 0) TWL_PHASE(6);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float lsum = l[h] * alpha[h];
@@ -382,7 +373,6 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
 #pragma unroll
     for (int h = 0; h < G; ++h) m[h] = row_bcast_f32(mh, h);
   }
-  TWL_PHASE(1);
   // Sum the token groups of each channel slice (same scale: m is shared by the wave). The
   // values are (l, acc[0..7]) per head; for d = 64 the two groups of a row are added first,
   // then the four rows are summed scattered, so each row ends with a quarter of the values
@@ -414,7 +404,6 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
     }
   }
   __syncthreads();
-  TWL_PHASE(2);
   // this chunk's (M, L, A) per head, merged over the waves
   for (int i = threadIdx.x; i < G * D; i += kDecThreads) {
     const int h = i / D, c = i % D;
@@ -438,9 +427,6 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
       part_o[pidx * D + c] = A;
     }
   }
-  TWL_PHASE(3);
-  TWL_PHASE_FLUSH(0, 32);
-  TWL_SPAN_END();
 }
 
 // Merge of the chunk partials when they are more than one: one wave per (sequence, query

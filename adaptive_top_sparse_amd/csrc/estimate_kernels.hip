@@ -15,9 +15,6 @@
 #include "twl_device.h"
 #include "twl_launch.h"
 
-TWL_PHASE_STORAGE(estimate)
-TWL_SPAN_STORAGE(estimate)
-
 namespace twl {
 namespace {
 
@@ -153,9 +150,6 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   __shared__ __attribute__((aligned(16))) f16 qs[G][D];
   __shared__ float qsum[G][NG];
   __shared__ float red_m[kEstWaves][G], red_l[kEstWaves][G];
-  TWL_PHASE_BEGIN(0, 32);
-  TWL_PHASE(0);
-  TWL_SPAN_BEGIN();
   const int b = blockIdx.z;
   const int g = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -299,7 +293,6 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   for (int i = 0; i < PB; ++i) keep_loaded(phys0[i]);
   load_codes(ids0, phys0, cw0, mw0);
   if (n_batches > 1) load_phys(1, ids1, phys1);
-  TWL_PHASE(1);
 
   uint32_t code_exp_v[5];  // code_exp(2i), held in VGPRs (vz is an opaque zero)
   const int vz = vgpr_zero();
@@ -393,7 +386,6 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
       for (int i = 0; i < PB; ++i) ids1[i] = ids2[i];
     }
   }
-  TWL_PHASE(2);
   // (max, sum exp) per head: over the row's 16 tokens, then over the waves
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
@@ -417,9 +409,6 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     for (int w2 = 0; w2 < kEstWaves; ++w2) L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * exp2_unit(red_m[w2][h] - M) : 0.f;
     partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(M, L);
   }
-  TWL_PHASE(3);
-  TWL_PHASE_FLUSH(0, 32);
-  TWL_SPAN_END();
 }
 
 // w = exp(s - M) / L with (M, L) merged from the row's chunk partials; invalid slots hold

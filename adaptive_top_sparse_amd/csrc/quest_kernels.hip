@@ -15,20 +15,11 @@
 #include "twl_device.h"
 #include "twl_launch.h"
 
-TWL_PHASE_STORAGE(quest)
-TWL_SPAN_STORAGE(quest)
-
 namespace twl {
 namespace {
 
 #ifndef TWL_SCORE_THREADS
 #define TWL_SCORE_THREADS 256
-#endif
-#ifndef TWL_SCORE_XCD_REMAP
-#define TWL_SCORE_XCD_REMAP 0
-#endif
-#ifndef TWL_SELECT_SMALL
-#define TWL_SELECT_SMALL 0
 #endif
 #ifndef TWL_SCORE_ROUNDS
 #define TWL_SCORE_ROUNDS 4
@@ -101,24 +92,8 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
   constexpr int ROUNDS = kScoreRounds;
   constexpr int PPB = PPI * ROUNDS;
   static_assert(ROUNDS == 4, "the round reduction handles four rounds");
-  TWL_PHASE_BEGIN(0, 4);
-  TWL_PHASE(0);
-  TWL_SPAN_BEGIN();
   const int b = blockIdx.z;
-  int bx = blockIdx.x, by = blockIdx.y;
-#if TWL_SCORE_XCD_REMAP
-  {
-    // work-groups are handed to the XCDs in turn; renumber them so that each XCD gets a
-    // contiguous share of the bounds (a permutation, so any placement stays correct)
-    const int nb = gridDim.x * gridDim.y;
-    if (nb % 8 == 0) {
-      const int lin = blockIdx.y * gridDim.x + blockIdx.x;
-      const int rl = (lin % 8) * (nb / 8) + lin / 8;
-      bx = rl % gridDim.x;
-      by = rl / gridDim.x;
-    }
-  }
-#endif
+  const int bx = blockIdx.x, by = blockIdx.y;
   const int g = by;
   const int Hq = Hkv * G;
   const int n = seq_len_clamped(seq_lens, b, max_pages);
@@ -161,7 +136,6 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
     A[c] = sA[c0 + c];
     Bc[c] = sB[c0 + c];
   }
-  TWL_PHASE(1);
   double part[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
@@ -180,9 +154,6 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
   const int p = p0 + round_of_lane<LPP>() * PPI + threadIdx.x / LPP;
   if (writes_round<LPP>() && p < P)
     scores[(static_cast<long>(b) * Hkv + g) * score_row_stride(max_pages) + p] = total;
-  TWL_PHASE(2);
-  TWL_PHASE_FLUSH(0, 4);
-  TWL_SPAN_END();
 }
 
 // One 1024-thread block per (sequence, KV head); thread t owns pages [t*KPT, t*KPT+KPT).
@@ -208,8 +179,6 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   __shared__ uint32_t n_short;
   __shared__ uint64_t short_key[kWave + 1];
   __shared__ int short_page[kWave + 1];
-  TWL_PHASE_BEGIN(4, 32);
-  TWL_PHASE(4);
   const int b = blockIdx.y;
   const int g = blockIdx.x;
   const long unit = static_cast<long>(b) * Hkv + g;
@@ -240,7 +209,6 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   if (threadIdx.x == 0) sel_count[unit] = m;
   if (m == P) {
     for (int i = threadIdx.x; i < P; i += NT) out[i] = i;
-    TWL_PHASE_FLUSH(4, 32);
     return;
   }
   // the first pass's histogram is cleared now; the barrier of the min/max reduction below
@@ -258,9 +226,7 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
       kmax = key[i] > kmax ? key[i] : kmax;
     }
   }
-  TWL_PHASE(5);
   block_minmax<NT, uint64_t>(kmin, kmax, red64, red64b, ~0ull, 0ull, &kmin, &kmax);
-  TWL_PHASE(6);
 
   // bits above `top` are common to every key
   uint64_t prefix = 0, mask = 0;
@@ -304,7 +270,6 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
       rem -= above;
       prefix |= static_cast<uint64_t>(digit) << lo_bit;
       mask |= dmask << lo_bit;
-      TWL_PHASE(7 + (npass < 4 ? npass : 4));
       ++npass;
       if (cnt == rem) {
         mode = kAllIn;
@@ -323,9 +288,7 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
             }
           }
         }
-        TWL_PHASE(14);
         __syncthreads();
-        TWL_PHASE(15);
         {
           // page i = lane; wave w counts the bucket's pages in its share that come before
           // page i in the selection order, then wave 0 totals the shares
@@ -347,7 +310,6 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
             r_part += (j < n_in && (kj > mk || (kj == mk && pj < mp))) ? 1u : 0u;
           }
           part[wv * kWave + l] = r_part;
-          TWL_PHASE(16);
           __syncthreads();
           if (wv == 0) {
             uint32_t rank = 0;
@@ -360,7 +322,6 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
           }
         }
         __syncthreads();
-        TWL_PHASE(17);
         mode = kPair;
         t_key = short_key[kWave];
         t_page = short_page[kWave];
@@ -404,12 +365,9 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
     n_sel += c ? 1u : 0u;
   }
   uint32_t pos = block_excl_scan_u32<NT>(n_sel, scan_lds, &tot);
-  TWL_PHASE(12);
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
     if (chosen[i]) out[pos++] = first + i;
-  TWL_PHASE(13);
-  TWL_PHASE_FLUSH(4, 32);
 }
 
 template <int NT, int KPT>
@@ -456,19 +414,6 @@ hipError_t launch_quest_scores(const Layout& L, const void* q, const void* minma
 
 hipError_t launch_quest_top(const Layout& L, const double* scores, int budget,
                             int32_t* sel_pages, int32_t* sel_count, hipStream_t s) {
-#if TWL_SELECT_SMALL > 0
-  // a tuning option, off by default: 256 threads (one wave per SIMD) up to this many pages
-  if (L.max_pages <= TWL_SELECT_SMALL) {
-    const int kpt = (L.max_pages + 255) / 256;
-    if (kpt <= 1) select_launch<256, 1>(L, budget, sel_pages, sel_count, scores, s);
-    else if (kpt <= 2) select_launch<256, 2>(L, budget, sel_pages, sel_count, scores, s);
-    else if (kpt <= 4) select_launch<256, 4>(L, budget, sel_pages, sel_count, scores, s);
-    else if (kpt <= 8) select_launch<256, 8>(L, budget, sel_pages, sel_count, scores, s);
-    else if (kpt <= 16) select_launch<256, 16>(L, budget, sel_pages, sel_count, scores, s);
-    else select_launch<256, 32>(L, budget, sel_pages, sel_count, scores, s);
-    return hipGetLastError();
-  }
-#endif
   const int kpt = (L.max_pages + 1023) / 1024;
   if (kpt <= 1) select_launch<1024, 1>(L, budget, sel_pages, sel_count, scores, s);
   else if (kpt <= 2) select_launch<1024, 2>(L, budget, sel_pages, sel_count, scores, s);

@@ -6,86 +6,6 @@
 
 #include "twl_launch.h"
 
-// Opt-in phase timing for tuning builds (-DTWL_PHASE_TIMING): thread 0 of work-group 0 of a
-// kernel stamps the 100 MHz real-time clock (and the shader clock at entry 32 + i) at
-// marked phase boundaries into LDS, and TWL_PHASE_FLUSH at the kernel's end copies the
-// stamps to a per-file device array that an exported twl_phase_<file>() copies out. The
-// stamps stay in LDS until the end because a global store before a block barrier would
-// make that barrier wait for the store to complete. Compiled out otherwise.
-#ifdef TWL_PHASE_TIMING
-__device__ __forceinline__ unsigned long long* twl_phase_lds() {
-  __shared__ unsigned long long ts[64];
-  return ts;
-}
-#define TWL_PHASE_STORAGE(NAME)                                                       \
-  static __device__ unsigned long long twl_phase_ts[64];                              \
-  extern "C" void twl_phase_##NAME(unsigned long long* host) {                        \
-    (void)hipMemcpyFromSymbol(host, HIP_SYMBOL(twl_phase_ts), sizeof(twl_phase_ts));  \
-  }
-// TWL_PHASE_BEGIN(lo, hi) at kernel entry clears the kernel's own stamp range [lo, hi)
-// (kernels of one file own disjoint ranges), TWL_PHASE_FLUSH(lo, hi) copies it out.
-#define TWL_PHASE_BEGIN(lo, hi)                                                        \
-  do {                                                                                 \
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {   \
-      for (int z_ = (lo); z_ < (hi); ++z_) twl_phase_lds()[z_] = twl_phase_lds()[32 + z_] = 0ull; \
-    }                                                                                  \
-  } while (0)
-#define TWL_PHASE(i)                                                                   \
-  do {                                                                                 \
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {   \
-      twl_phase_lds()[i] = __builtin_amdgcn_s_memrealtime();                           \
-      twl_phase_lds()[32 + (i)] = __builtin_amdgcn_s_memtime();                        \
-    }                                                                                  \
-  } while (0)
-#define TWL_PHASE_FLUSH(lo, hi)                                                        \
-  do {                                                                                 \
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {   \
-      for (int z_ = (lo); z_ < (hi); ++z_) {                                           \
-        twl_phase_ts[z_] = twl_phase_lds()[z_];                                        \
-        twl_phase_ts[32 + z_] = twl_phase_lds()[32 + z_];                              \
-      }                                                                                \
-    }                                                                                  \
-  } while (0)
-// start and end clock of every work-group (linear id < 32768) and the XCC it ran on
-#define TWL_SPAN_STORAGE(NAME)                                                         \
-  static __device__ unsigned long long twl_span_ts[3 * 32768];                         \
-  extern "C" void twl_span_##NAME(unsigned long long* host) {                          \
-    (void)hipMemcpyFromSymbol(host, HIP_SYMBOL(twl_span_ts), sizeof(twl_span_ts));     \
-  }
-#define TWL_BLOCK_LINEAR() \
-  ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x)
-#define TWL_SPAN_BEGIN()                                                               \
-  do {                                                                                 \
-    if (threadIdx.x == 0 && TWL_BLOCK_LINEAR() < 32768) {                              \
-      twl_span_ts[3 * TWL_BLOCK_LINEAR()] = __builtin_amdgcn_s_memrealtime();          \
-      twl_span_ts[3 * TWL_BLOCK_LINEAR() + 2] = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)); \
-    }                                                                                  \
-  } while (0)
-#define TWL_SPAN_END()                                                                 \
-  do {                                                                                 \
-    if (threadIdx.x == 0 && TWL_BLOCK_LINEAR() < 32768)                                \
-      twl_span_ts[3 * TWL_BLOCK_LINEAR() + 1] = __builtin_amdgcn_s_memrealtime();      \
-  } while (0)
-#else
-#define TWL_SPAN_STORAGE(NAME)
-#define TWL_SPAN_BEGIN() \
-  do {                   \
-  } while (0)
-#define TWL_SPAN_END() \
-  do {                 \
-  } while (0)
-#define TWL_PHASE_STORAGE(NAME)
-#define TWL_PHASE_BEGIN(lo, hi) \
-  do {                          \
-  } while (0)
-#define TWL_PHASE(i) \
-  do {               \
-  } while (0)
-#define TWL_PHASE_FLUSH(lo, hi) \
-  do {                          \
-  } while (0)
-#endif
-
 namespace twl {
 
 constexpr int kWave = 64;
