@@ -21,13 +21,15 @@ TWL_ERR_INVALID_ARG = -1
 TWL_ERR_UNSUPPORTED = -2
 TWL_ERR_WORKSPACE = -3
 TWL_ERR_LAUNCH = -4
+TWL_ERR_SCRATCH = -5
 
 EXPORTED = ("twilight_quantize_keys", "quest_page_bounds", "quest_select_pages",
             "twilight_estimate_weights", "twilight_topp_select", "twilight_sparse_decode",
             "twilight_append_keys", "twilight_topp_select_headwise",
             "twilight_sparse_decode_headwise", "twilight_estimate_topp",
             "twilight_estimate_topp_headwise", "quest_page_scores", "quest_top_pages",
-            "quest_score_stride", "twilight_workspace_size", "twilight_status_string")
+            "twilight_sparse_decode_noalloc", "quest_score_stride",
+            "twilight_workspace_size", "twilight_status_string")
 
 
 class TwilightError(RuntimeError):
@@ -71,7 +73,8 @@ def lib():
         L.twilight_estimate_topp_headwise.argtypes = L.twilight_estimate_topp.argtypes
         L.quest_page_scores.argtypes = [LP, P, P, P, P]
         L.quest_top_pages.argtypes = [LP, P, I32, P, P, P]
-        for name in EXPORTED[:13]:
+        L.twilight_sparse_decode_noalloc.argtypes = [LP, P, P, P, P, P, I32, F, P, P]
+        for name in EXPORTED[:14]:
             getattr(L, name).restype = ctypes.c_int
         L.quest_score_stride.argtypes = [I32]
         L.quest_score_stride.restype = ctypes.c_int64
@@ -301,6 +304,20 @@ def twilight_sparse_decode(layout: Layout, q, k_cache, v_cache, kept, kept_count
     """Group-wise kept lists [B, Hkv, kept_stride]."""
     _sparse_decode("twilight_sparse_decode", layout, q, k_cache, v_cache, kept, kept_count,
                    kept_stride, sm_scale, out, workspace, stream)
+
+
+def twilight_sparse_decode_noalloc(layout: Layout, q, k_cache, v_cache, kept, kept_count,
+                                   kept_stride: int, sm_scale: float, out,
+                                   stream=None) -> None:
+    """Group-wise decode with the library's fixed device scratch (no workspace, no
+    allocation; calls that overlap on one GPU race)."""
+    import torch
+    st = lib().twilight_sparse_decode_noalloc(
+        ctypes.byref(layout), _ptr(q, torch.float16, "q"), _ptr(k_cache, torch.float16, "k_cache"),
+        _ptr(v_cache, torch.float16, "v_cache"), _ptr(kept, torch.int32, "kept"),
+        _ptr(kept_count, torch.int32, "kept_count"), int(kept_stride), float(sm_scale),
+        _ptr(out, torch.float16, "out"), _stream(stream))
+    _check("twilight_sparse_decode_noalloc", st)
 
 
 def twilight_sparse_decode_headwise(layout: Layout, q, k_cache, v_cache, kept, kept_count,

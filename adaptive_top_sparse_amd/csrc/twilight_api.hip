@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/twilight.h"
 #include "twl_launch.h"
@@ -95,15 +96,14 @@ int topp_select(bool headwise, const twl_layout_t* L, const float* weights,
                                         p, kept, kept_count, tau, workspace, stream));
 }
 
-int sparse_decode(bool headwise, const twl_layout_t* L, const void* q, const void* k_cache,
-                  const void* v_cache, const int32_t* kept, const int32_t* kept_count,
-                  int32_t kept_stride, float sm_scale, void* out, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
-  Layout lay{};
-  bool empty = false;
-  int st = check_layout(L, &lay, &empty);
+// Host checks of a decode call's arguments other than its workspace.
+int check_decode(bool headwise, const twl_layout_t* L, const void* q, const void* k_cache,
+                 const void* v_cache, const int32_t* kept, const int32_t* kept_count,
+                 int32_t kept_stride, float sm_scale, const void* out, Layout* lay,
+                 bool* empty) {
+  int st = check_layout(L, lay, empty);
   if (st != TWL_OK) return st;
-  lay.headwise = headwise;
+  lay->headwise = headwise;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || kept == nullptr ||
       kept_count == nullptr || out == nullptr)
     return TWL_ERR_INVALID_ARG;
@@ -112,12 +112,44 @@ int sparse_decode(bool headwise, const twl_layout_t* L, const void* q, const voi
     return TWL_ERR_INVALID_ARG;
   if (kept_stride < 1 || !std::isfinite(sm_scale)) return TWL_ERR_INVALID_ARG;
   if (static_cast<int64_t>(kept_stride) > twl::kToppMaxSlots * 64) return TWL_ERR_UNSUPPORTED;
+  return TWL_OK;
+}
+
+int sparse_decode(bool headwise, const twl_layout_t* L, const void* q, const void* k_cache,
+                  const void* v_cache, const int32_t* kept, const int32_t* kept_count,
+                  int32_t kept_stride, float sm_scale, void* out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  Layout lay{};
+  bool empty = false;
+  const int st = check_decode(headwise, L, q, k_cache, v_cache, kept, kept_count, kept_stride,
+                              sm_scale, out, &lay, &empty);
+  if (st != TWL_OK) return st;
   if (empty) return TWL_OK;
   if (workspace == nullptr || !aligned16(workspace) ||
       workspace_bytes < twl::decode_workspace_bytes(lay, kept_stride))
     return TWL_ERR_WORKSPACE;
   return launch_status(twl::launch_sparse_decode(lay, q, k_cache, v_cache, kept, kept_count,
                                                  kept_stride, sm_scale, out, workspace, stream));
+}
+
+// Fixed device scratch of twilight_sparse_decode_noalloc, for callers that cannot
+// allocate. In host code `scratch` is only a stand-in for the symbol: its device address is
+// looked up once per device (with that device current) and kept in scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_ptr[kMaxDevices];
+
+// The current device's copy of the scratch array, or nullptr when it cannot be found.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) scratch_ptr[dev] = p;
+  });
+  return scratch_ptr[dev];
 }
 
 }  // namespace
@@ -131,6 +163,7 @@ const char* twilight_status_string(int status) {
     case TWL_ERR_UNSUPPORTED: return "unsupported shape (head_dim, group size, page size or extent)";
     case TWL_ERR_WORKSPACE: return "workspace missing or too small";
     case TWL_ERR_LAUNCH: return "kernel launch failed";
+    case TWL_ERR_SCRATCH: return "the call needs more than the fixed 16 MiB no-allocation scratch";
     default: return "unknown status";
   }
 }
@@ -354,6 +387,25 @@ int twilight_sparse_decode(const twl_layout_t* L, const void* q, const void* k_c
                            size_t workspace_bytes, hipStream_t stream) {
   return sparse_decode(false, L, q, k_cache, v_cache, kept, kept_count, kept_stride, sm_scale,
                        out, workspace, workspace_bytes, stream);
+}
+
+int twilight_sparse_decode_noalloc(const twl_layout_t* L, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* kept,
+                                   const int32_t* kept_count, int32_t kept_stride,
+                                   float sm_scale, void* out, hipStream_t stream) {
+  // every host check, the size limit included, comes before the device query
+  Layout lay{};
+  bool empty = false;
+  const int st = check_decode(false, L, q, k_cache, v_cache, kept, kept_count, kept_stride,
+                              sm_scale, out, &lay, &empty);
+  if (st != TWL_OK) return st;
+  if (empty) return TWL_OK;
+  if (twl::decode_workspace_bytes(lay, kept_stride) > kNoAllocScratchBytes)
+    return TWL_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (ws == nullptr) return TWL_ERR_LAUNCH;
+  return launch_status(twl::launch_sparse_decode(lay, q, k_cache, v_cache, kept, kept_count,
+                                                 kept_stride, sm_scale, out, ws, stream));
 }
 
 int twilight_sparse_decode_headwise(const twl_layout_t* L, const void* q, const void* k_cache,

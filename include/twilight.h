@@ -63,7 +63,9 @@ typedef enum {
   TWL_ERR_INVALID_ARG = -1, /* null or misaligned pointer, bad size or value */
   TWL_ERR_UNSUPPORTED = -2, /* a shape the library has no kernel for */
   TWL_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  TWL_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
+  TWL_ERR_LAUNCH = -4,      /* the HIP runtime rejected a kernel launch */
+  TWL_ERR_SCRATCH = -5      /* the call needs more scratch than the fixed device buffer of
+                               twilight_sparse_decode_noalloc holds */
 } twl_status_t;
 
 typedef struct twl_layout {
@@ -245,6 +247,21 @@ int twilight_sparse_decode_headwise(const twl_layout_t* L, const void* q, const 
                                     const int32_t* kept_count, int32_t kept_stride,
                                     float sm_scale, void* out, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/* twilight_sparse_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same kernels
+ * and results, with the split-KV partials in a fixed 16 MiB device buffer that the library
+ * owns (one per GPU, held until the process ends) instead of a caller's workspace. The call
+ * allocates and frees nothing. Its partials need B * Hq * chunks * (d + 2) * 4 bytes, with
+ * chunks = ceil(kept_stride / chunk tokens) as the decode splits the lists (for example
+ * 2.1 MB for B = 1, Hq = 32, d = 128, kept_stride = 8192); a call that needs more returns
+ * TWL_ERR_SCRATCH with nothing enqueued. Every call on one GPU shares that GPU's buffer:
+ * calls that overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller. Other arguments and errors as twilight_sparse_decode. */
+int twilight_sparse_decode_noalloc(const twl_layout_t* L, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* kept,
+                                   const int32_t* kept_count, int32_t kept_stride,
+                                   float sm_scale, void* out, hipStream_t stream);
 
 /* Workspace bytes that every call above needs for this layout when candidate and kept
  * lists have cand_stride_pages pages (kept_stride = cand_stride_pages * 16). One

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert twl.status_string(0) == "ok"
-    for st in (-1, -2, -3, -4):
+    for st in (-1, -2, -3, -4, -5):
         assert twl.status_string(st) and twl.status_string(st) != "unknown status"
     assert twl.status_string(12345) == "unknown status"
 
@@ -139,6 +139,30 @@ def test_newer_entry_points_reject_invalid_arguments_on_the_host():
     bad.key_bits = 3
     assert _call("twilight_quantize_keys", ctypes.byref(bad), FAKE, None, FAKE, FAKE, None) == twl.TWL_ERR_UNSUPPORTED
     assert twl.twilight_workspace_size(bad, 64) == 0
+
+
+def test_noalloc_decode_checks_arguments_and_its_fixed_scratch_on_the_host():
+    # the no-allocation decode takes no workspace: the usual argument checks, then a
+    # refusal (nothing enqueued) when the partials would not fit its fixed 16 MiB buffer;
+    # all of it before any device query, so it answers without a GPU
+    f = ctypes.c_float
+    Lp = ctypes.byref(layout())
+    assert _call("twilight_sparse_decode_noalloc", Lp, None, FAKE, FAKE, FAKE, FAKE, 1024, f(0.1),
+                 FAKE, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("twilight_sparse_decode_noalloc", Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 0, f(0.1),
+                 FAKE, None) == twl.TWL_ERR_INVALID_ARG
+    assert _call("twilight_sparse_decode_noalloc", Lp, FAKE, FAKE, FAKE, FAKE, FAKE, 1024,
+                 f(float("nan")), FAKE, None) == twl.TWL_ERR_INVALID_ARG
+    # B = 64 sequences of 32 heads with 64k-token kept lists need far more than 16 MiB
+    big = layout(B=64, Hq=32, Hkv=8, max_pages=4096, phys=64 * 4096)
+    assert _call("twilight_sparse_decode_noalloc", ctypes.byref(big), FAKE, FAKE, FAKE, FAKE,
+                 FAKE, 65536, f(0.1), FAKE, None) == twl.TWL_ERR_SCRATCH
+    assert "16 MiB" in twl.status_string(twl.TWL_ERR_SCRATCH)
+    e = layout(B=0)
+    e.page_table = None
+    e.seq_lens = None
+    assert _call("twilight_sparse_decode_noalloc", ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE,
+                 1024, f(0.1), FAKE, None) == twl.TWL_OK
 
 
 def test_unsupported_shapes_are_reported():
