@@ -30,6 +30,15 @@ HBM_PEAK = 8.0e12            # MI355X HBM3E, bytes/s
 PAGE = 16
 
 
+# the kernels behind each call of the step, in launch order
+CALL_KERNELS = {
+    "quest_page_scores": ("quest_score_kernel",),
+    "quest_top_pages": ("quest_select_kernel",),
+    "twilight_estimate_topp": ("estimate_logits_kernel", "topp_kernel"),
+    "twilight_sparse_decode": ("sparse_decode_kernel", "decode_merge_kernel"),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -38,7 +47,7 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--replicas", type=int, default=16)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the dense and Quest-only comparison steps")
@@ -365,53 +374,119 @@ def time_two_bit(w, p, stream, steps, warmup, replicas, buf4):
             "kept_set_jaccard_2bit_vs_4bit": float(np.mean(jac))}
 
 
-def cpu_baseline(w, p, seconds):
-    """The fp64 oracle (stages select, estimate, top-p, attention; the cache is quantized
-    beforehand, as on the GPU) on whole decode steps of the same workload, single thread,
-    repeated until `seconds` have passed."""
+def cpu_info():
+    """Host CPU model name and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return model, usable
+
+
+def _oracle_unit_prep(w, units):
+    """Per (sequence, KV head) unit, the quantized keys and page bounds the step reads
+    (cache maintenance, done before timing, as on the GPU)."""
     import oracle
-    s = w.spec
-    G = s.G
-    sm = float(np.float32(1.0 / math.sqrt(s.d)))
-    # a bounded sample: the first two (sequence, KV head) units of the step
-    units = [(b, g) for b in range(s.B) for g in range(s.Hkv)][:2]
     prep = {}
     for b, g in units:
         k = w.k[b][g]
         codes, scale, zero = oracle.quantize_keys(k)
         lo, hi = oracle.page_bounds(k) if w.budget is not None else (None, None)
         prep[(b, g)] = (codes, scale, zero, lo, hi)
-    cand_total = 0
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        for b, g in units:
-            codes, scale, zero, lo, hi = prep[(b, g)]
-            qg = w.q[b, g * G:(g + 1) * G]
-            n = int(w.seq_lens[b])
-            if w.budget is not None:
-                sel = oracle.quest_select(qg, lo, hi, w.budget)
-                n_slots = w.budget * PAGE
-                tok = np.repeat(sel.astype(np.int64), PAGE) * PAGE + np.tile(np.arange(PAGE), len(sel))
-                valid = np.zeros(n_slots, bool)
-                valid[:tok.size] = tok < n
-            else:
-                sel = None
-                n_slots = -(-n // PAGE) * PAGE
-                valid = np.arange(n_slots) < n
-            wts = oracle.estimate_weights(qg, codes, scale, zero, n, sel, n_slots, sm)
-            kept, _ = oracle.topp_select(wts, valid, p, sel)
-            oracle.sparse_attention(qg, w.k[b][g], w.v[b][g], kept, sm)
-            cand_total += int(valid.sum())
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": cand_total / el, "unit": "candidate tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{steps} passes over {len(units)} (sequence, KV head) units of the "
-                      f"same workload (select, estimate, top-p, attention), single-threaded "
-                      f"fp64 oracle, {el:.1f} s; cache quantization excluded"}
+    return prep
+
+
+def _oracle_unit_step(w, p, b, g, prep, sm):
+    """One unit of a decode step in the oracle: Quest select, estimate, top-p, attention.
+    Returns its candidate count."""
+    import oracle
+    G = w.spec.G
+    codes, scale, zero, lo, hi = prep
+    qg = w.q[b, g * G:(g + 1) * G]
+    n = int(w.seq_lens[b])
+    if n == 0:
+        return 0
+    if w.budget is not None:
+        sel = oracle.quest_select(qg, lo, hi, w.budget)
+        n_slots = w.budget * PAGE
+        tok = np.repeat(sel.astype(np.int64), PAGE) * PAGE + np.tile(np.arange(PAGE), len(sel))
+        valid = np.zeros(n_slots, bool)
+        valid[:tok.size] = tok < n
+    else:
+        sel = None
+        n_slots = -(-n // PAGE) * PAGE
+        valid = np.arange(n_slots) < n
+    wts = oracle.estimate_weights(qg, codes, scale, zero, n, sel, n_slots, sm)
+    kept, _ = oracle.topp_select(wts, valid, p, sel)
+    oracle.sparse_attention(qg, w.k[b][g], w.v[b][g], kept, sm)
+    return int(valid.sum())
+
+
+def cpu_baseline(w, p, seconds, max_threads=16):
+    """The fp64 oracle on whole decode steps of the same workload (every (sequence, KV head)
+    unit of the step: Quest select, estimate, top-p, attention; the cache is quantized
+    beforehand, as on the GPU), timed on the host cores, first single-threaded, then with
+    one thread per unit across the cores this process may use (at most `max_threads`; the
+    oracle's C functions release the interpreter lock, so the threads run in parallel).
+    Each variant repeats whole steps until `seconds` have passed (at least one step); on
+    the large batched workloads a bounded sample of the step's units is timed instead, as
+    the sample field says."""
+    import concurrent.futures
+    s = w.spec
+    sm = float(np.float32(1.0 / math.sqrt(s.d)))
+    model, usable = cpu_info()
+    threads = max(1, min(max_threads, usable))
+    units = [(b, g) for b in range(s.B) for g in range(s.Hkv)]
+    # about one second of single-threaded work per unit sample keeps the default run short
+    sample = units
+    if len(units) > 64:
+        rng = np.random.default_rng(0)
+        sample = [units[i] for i in sorted(rng.choice(len(units), 64, replace=False))]
+    prep = _oracle_unit_prep(w, sample)
+
+    def one_step(pool):
+        if pool is None:
+            return sum(_oracle_unit_step(w, p, b, g, prep[(b, g)], sm) for b, g in sample)
+        futs = [pool.submit(_oracle_unit_step, w, p, b, g, prep[(b, g)], sm) for b, g in sample]
+        return sum(f.result() for f in futs)
+
+    res = {}
+    for name, nthr in (("single", 1), ("multi", threads)):
+        pool = concurrent.futures.ThreadPoolExecutor(nthr) if nthr > 1 else None
+        cand, steps = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            cand += one_step(pool)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds / 2:
+                break
+        if pool is not None:
+            pool.shutdown()
+        res[name] = {"value": cand / el, "threads": nthr, "steps": steps, "seconds": el,
+                     "step_ms": el / steps * 1e3}
+    scope = ("every (sequence, KV head) unit of the step" if sample is units else
+             f"{len(sample)} of the step's {len(units)} (sequence, KV head) units, seeded choice")
+    return {"value": res["multi"]["value"], "unit": "candidate tokens/s",
+            "cores": res["multi"]["threads"], "kind": "oracle",
+            "sample": f"{res['multi']['steps']} passes over {scope} (Quest select, estimate, "
+                      f"top-p, attention), fp64 oracle, one thread per unit on "
+                      f"{res['multi']['threads']} threads, {res['multi']['seconds']:.1f} s; "
+                      f"cache quantization excluded",
+            "single_thread": {"value": res["single"]["value"], "cores": 1,
+                              "steps": res["single"]["steps"],
+                              "step_ms": res["single"]["step_ms"]},
+            "multi_thread_step_ms": res["multi"]["step_ms"],
+            "cpu_model": model, "usable_cores": usable, "units_per_step": len(sample)}
 
 
 def main():
@@ -528,15 +603,60 @@ def main():
     torch.cuda.synchronize()
     graph_ms = g0.elapsed_time(g1) / args.steps
 
+    # the same replays with one event between consecutive steps: the distribution of step
+    # times (each recorded event adds a little to the step it closes)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    with torch.cuda.stream(stream):
+        sev[0].record(stream)
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+            sev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step_us = np.array([sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(args.steps)])
+
+    # the pruner and the sparse decode (stages a2-a5) alone, on the selection the step made:
+    # one graph of the fused estimate + top-p call and the decode call for every replica in
+    # turn (back-to-back launches, as each call alone is timed above)
+    a25 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(a25, stream=stream):
+        for r in range(len(reps)):
+            pipeline.run_step(reps[r], bufs[r], p, stream=stream,
+                              stages=("estimate", "topp", "decode"))
+    with torch.cuda.stream(stream):
+        a25.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, args.steps // len(reps))
+    with torch.cuda.stream(stream):
+        g0.record(stream)
+        for _ in range(n_rep):
+            a25.replay()
+        g1.record(stream)
+    torch.cuda.synchronize()
+    a25_ms = g0.elapsed_time(g1) / (n_rep * len(reps))
+    del a25
+
     per_stage_bytes, cand, kept = stage_bytes(base, bufs[0], base.d)
     step_bytes = sum(per_stage_bytes.values())
-    dom = max(per_stage_bytes, key=lambda k: per_stage_bytes[k])
-    achieved = per_stage_bytes[dom] / (call_ms[dom] * 1e-3)
     stream_bw = stream_bandwidth(stream)
-    roofline = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK, "traffic": measured_traffic(dom, args.config, p), "kernel": dom,
-                "bytes_per_launch": per_stage_bytes[dom], "avg_launch_us": call_ms[dom] * 1e3,
-                "measured_stream": stream_bw / 1e9, "frac_of_measured_stream": achieved / stream_bw}
+
+    def roof(call):
+        achieved = per_stage_bytes[call] / (call_ms[call] * 1e-3)
+        return {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                "traffic": measured_traffic(call, args.config, p), "kernel": call,
+                "kernels": list(CALL_KERNELS[call]),
+                "bytes_per_launch": per_stage_bytes[call], "avg_launch_us": call_ms[call] * 1e3,
+                "measured_stream": stream_bw / 1e9,
+                "frac_of_measured_stream": achieved / stream_bw}
+
+    # the roofline is reported for the call that takes the most device time per step (each
+    # call of the step timed alone, as back-to-back launches in a graph), and for the Quest
+    # page scorer, the kernel that moves the most bytes, when the workload has one
+    dom = max(call_ms, key=lambda k: call_ms[k])
+    roofline = roof(dom)
+    roofline["chosen_by"] = "device time per step"
+    a25_bytes = per_stage_bytes["twilight_estimate_topp"] + per_stage_bytes["twilight_sparse_decode"]
+    a25_rate = a25_bytes / (a25_ms * 1e-3)
     step_s = graph_ms * 1e-3
     res = {
         "metric": METRIC,
@@ -557,8 +677,18 @@ def main():
                                f"Quest budget={w.budget} pages, p={p}",
                    "config_id": args.config, "p": p, "layer_replicas": len(reps),
                    "launch": "hipGraph per step"},
+        "step_us_median": float(np.median(per_step_us)),
+        "step_us_p90": float(np.percentile(per_step_us, 90)),
+        "step_us_events_mean": float(per_step_us.mean()),
         "hbm_frac_step": step_bytes / step_s / HBM_PEAK,
         "step_bytes": step_bytes,
+        "pruner_and_decode": {
+            "stages": "estimate + top-p + compaction + sparse decode (a2-a5)",
+            "calls": ["twilight_estimate_topp", "twilight_sparse_decode"],
+            "us": a25_ms * 1e3, "bytes": a25_bytes, "achieved_GBps": a25_rate / 1e9,
+            "frac": a25_rate / HBM_PEAK, "frac_of_measured_stream": a25_rate / stream_bw,
+            "us_at_70pct_of_peak": a25_bytes / (0.7 * HBM_PEAK) * 1e6},
+        "roofline_scorer": roof("quest_page_scores") if "quest_page_scores" in call_ms else None,
         "candidates": cand,
         "kept": kept,
         "plain_launch_us_per_step": plain_ms * 1e3,
