@@ -8,7 +8,9 @@ the L2 from serving a step out of cache, consecutive steps rotate over independe
 replicas (distinct buffers), as consecutive layers of a real decode do.
 
 Prints ONE JSON line. `value` is candidate tokens per second: sum over (sequence, KV head)
-of the candidate count, divided by the step time (hipGraph launch).
+of the candidate count, divided by the step time, with the steps of the layer replicas
+captured back to back in one hipGraph as a decode loop runs them (single-step graphs are
+reported beside it).
 """
 from __future__ import annotations
 
@@ -162,16 +164,17 @@ def stage_bytes(c, buf, d):
 
 
 def time_baselines(reps, bufs, stream, steps, warmup, twilight_us):
-    """Dense and Quest-only decode steps on the same kernels, hipGraph replays in rotation
-    over the same layer replicas: dense = twilight_sparse_decode over every token; Quest-only
-    = quest_select_pages + twilight_sparse_decode over every token of the selected pages."""
+    """Dense and Quest-only decode steps on the same kernels, timed like the Twilight step
+    (the layer replicas' steps in one hipGraph): dense = twilight_sparse_decode over every
+    token; Quest-only = quest_select_pages + twilight_sparse_decode over every token of the
+    selected pages."""
     import torch
     import adaptive_top_sparse_amd as twl
     from adaptive_top_sparse_amd import pipeline
     out = {"twilight_us": twilight_us}
     modes = ["dense"] + (["quest"] if reps[0].budget is not None else [])
     for mode in modes:
-        graphs, keep = [], []
+        runs, keep = [], []
         for c, buf in zip(reps, bufs):
             kept, count, stride = pipeline.baseline_kept(c, buf, mode)
             lay = c.layout()
@@ -186,65 +189,36 @@ def time_baselines(reps, bufs, stream, steps, warmup, twilight_us):
                                            buf.sel_count, ws, stream=stream)
                 twl.twilight_sparse_decode(lay, c.q, c.k_cache, c.v_cache, kept, count, stride,
                                            pipeline.default_sm_scale(c.d), o, ws, stream=stream)
-            with torch.cuda.stream(stream):
-                run()
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                run()
-            graphs.append(g)
-        with torch.cuda.stream(stream):
-            for i in range(warmup):
-                graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for i in range(steps):
-                graphs[i % len(graphs)].replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / steps * 1e3
+            runs.append(run)
+        us = layers_us(runs, stream, steps, warmup)
         name = "dense_us" if mode == "dense" else "quest_only_us"
         out[name] = us
         out["speedup_vs_" + ("dense" if mode == "dense" else "quest")] = us / twilight_us
-        del graphs, keep
+        del runs, keep
     out["note"] = ("same decode kernel; Quest-only token lists expanded once outside the "
                    "timed region (fixed q)")
     return out
 
 
 def time_append_and_layers(reps, bufs, p, stream, steps, warmup, layers=32):
-    """Two views of a real decode loop, hipGraph replays: the step with its per-token cache
-    maintenance first (quantize the newest token, recompute its page's bounds), and one
-    graph of `layers` such steps over the rotating replicas (a whole model's attention
-    layers), reported per layer."""
+    """Two views of a real decode loop: the step with its per-token cache maintenance first
+    (quantize the newest token, recompute its page's bounds), timed like the plain step (the
+    layer replicas' steps in one hipGraph), and one graph of `layers` such steps over the
+    rotating replicas (a whole model's attention layers), reported per layer."""
     import torch
     from adaptive_top_sparse_amd import pipeline
     R = len(reps)
-    graphs = []
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            pipeline.run_step(reps[r], bufs[r], p, stream=stream, append=True)
-        graphs.append(g)
+    step_us = layers_us([lambda r=r: pipeline.run_step(reps[r], bufs[r], p, stream=stream,
+                                                       append=True) for r in range(R)],
+                        stream, steps, warmup)
     big = torch.cuda.CUDAGraph()
     with torch.cuda.graph(big, stream=stream):
         for i in range(layers):
             pipeline.run_step(reps[i % R], bufs[i % R], p, stream=stream, append=True)
     with torch.cuda.stream(stream):
-        for i in range(warmup):
-            graphs[i % R].replay()
         big.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for i in range(steps):
-            graphs[i % R].replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    step_us = e0.elapsed_time(e1) / steps * 1e3
     n_big = max(1, steps // layers)
     with torch.cuda.stream(stream):
         e0.record(stream)
@@ -259,56 +233,50 @@ def time_append_and_layers(reps, bufs, p, stream, steps, warmup, layers=32):
 
 def time_headwise(reps, bufs, p, stream, steps, warmup):
     """The step with head-wise top-p and decode (a kept set per query head instead of one per
-    KV-head group), hipGraph replays in rotation over the same replicas, with the kept
+    KV-head group), timed like the group-wise step over the same replicas, with the kept
     token-heads of both modes (a group-wise kept token counts once per query head)."""
-    import torch
     from adaptive_top_sparse_amd import pipeline
     hbufs = [pipeline.alloc_step(c, headwise=True) for c in reps]
-    graphs = []
-    for c, hb in zip(reps, hbufs):
-        with torch.cuda.stream(stream):
-            pipeline.run_step(c, hb, p, stream=stream, headwise=True)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            pipeline.run_step(c, hb, p, stream=stream, headwise=True)
-        graphs.append(g)
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for i in range(steps):
-            graphs[i % len(graphs)].replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
+    us = layers_us([lambda c=c, hb=hb: pipeline.run_step(c, hb, p, stream=stream, headwise=True)
+                    for c, hb in zip(reps, hbufs)], stream, steps, warmup)
     G = reps[0].Hq // reps[0].Hkv
-    return {"headwise_step_us": e0.elapsed_time(e1) / steps * 1e3,
+    return {"headwise_step_us": us,
             "kept_token_heads_headwise": int(hbufs[0].kept_count.sum().item()),
             "kept_token_heads_groupwise": int(bufs[0].kept_count.sum().item()) * G}
 
 
-def _replay_us(graphs, stream, steps, warmup):
+def layers_us(runs, stream, steps, warmup):
+    """Device time per step of `runs` (one callable per layer replica, each enqueueing one
+    step on `stream`), captured back to back in one hipGraph as a decode loop runs them and
+    replayed until about `steps` steps have run."""
     import torch
     with torch.cuda.stream(stream):
-        for i in range(warmup):
-            graphs[i % len(graphs)].replay()
+        for run in runs:
+            run()
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for run in runs:
+            run()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup // len(runs))):
+            g.replay()
+    torch.cuda.synchronize()
+    n = max(1, steps // len(runs))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for i in range(steps):
-            graphs[i % len(graphs)].replay()
+        for _ in range(n):
+            g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps * 1e3
+    del g
+    return e0.elapsed_time(e1) / (n * len(runs)) * 1e3
 
 
 def time_two_bit(w, p, stream, steps, warmup, replicas, buf4):
     """The 2-bit key cache the pages ablate (4-bit keeps the estimated weights more stable):
-    the step on its own layer replicas (hipGraph replays in rotation), and the stability of
+    the step on its own layer replicas (timed like the 4-bit step), and the stability of
     both widths' kept sets on the first replica, measured against the exact weights
     (softmax of q.k on the fp16 keys over the same candidates, fp64, group mean): the exact
     mass each kept set captures (p is the target) and the overlap of the two sets."""
@@ -326,21 +294,13 @@ def time_two_bit(w, p, stream, steps, warmup, replicas, buf4):
     replicas = max(2, min(replicas, fit + 1))
     reps = [base] + [base.clone() for _ in range(replicas - 1)]
     bufs = [pipeline.alloc_step(r) for r in reps]
-    graphs = []
-    for c, b in zip(reps, bufs):
-        with torch.cuda.stream(stream):
-            pipeline.run_step(c, b, p, stream=stream)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            pipeline.run_step(c, b, p, stream=stream)
-        graphs.append(g)
-    us = _replay_us(graphs, stream, steps, warmup)
+    us = layers_us([lambda c=c, b=b: pipeline.run_step(c, b, p, stream=stream)
+                    for c, b in zip(reps, bufs)], stream, steps, warmup)
     k2, c2 = bufs[0].kept.cpu().numpy(), bufs[0].kept_count.cpu().numpy()
     k4, c4 = buf4.kept.cpu().numpy(), buf4.kept_count.cpu().numpy()
     sel = None if buf4.sel_pages is None else buf4.sel_pages.cpu().numpy()
     sel_n = None if buf4.sel_count is None else buf4.sel_count.cpu().numpy()
-    del graphs, bufs, reps, base
+    del bufs, reps, base
     torch.cuda.empty_cache()
     G = s.G
     sm = pipeline.default_sm_scale(s.d)
@@ -583,36 +543,67 @@ def main():
         call_ms[nm] = c0.elapsed_time(c1) / (n_rep * len(reps))
         del cg
 
-    # hipGraph: one captured step per replica, replayed in rotation (the timed number)
+    # hipGraph, as a decode loop runs the path: the steps of all R layer replicas captured
+    # back to back in one graph (the way a model's whole decode step is captured), so that
+    # the time is the stages' device time and not R graph launches. K steps are K // R
+    # replays of it and K % R single-step graphs (one captured step per replica, replayed in
+    # rotation, also timed alone below).
+    R = len(reps)
     graphs = []
-    for r in range(len(reps)):
+    for r in range(R):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             pipeline.run_step(reps[r], bufs[r], p, stream=stream)
         graphs.append(g)
+    layers = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(layers, stream=stream):
+        for r in range(R):
+            pipeline.run_step(reps[r], bufs[r], p, stream=stream)
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
+            graphs[i % R].replay()
+        layers.replay()
     torch.cuda.synchronize()
+    n_layers, n_rest = divmod(args.steps, R)
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         g0.record(stream)
-        for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
+        for _ in range(n_layers):
+            layers.replay()
+        for i in range(n_rest):
+            graphs[i].replay()
         g1.record(stream)
     torch.cuda.synchronize()
     graph_ms = g0.elapsed_time(g1) / args.steps
 
-    # the same replays with one event between consecutive steps: the distribution of step
-    # times (each recorded event adds a little to the step it closes)
+    # one graph launch per step: the same steps, each its own graph
+    with torch.cuda.stream(stream):
+        g0.record(stream)
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        g1.record(stream)
+    torch.cuda.synchronize()
+    single_graph_ms = g0.elapsed_time(g1) / args.steps
+
+    # the distribution of step times: one event between consecutive R-step replays (each
+    # replay's time over R), and one between consecutive single-step replays (each recorded
+    # event adds a little to the step it closes)
+    n_dist = max(20, args.steps // R)
+    lev = [torch.cuda.Event(enable_timing=True) for _ in range(n_dist + 1)]
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with torch.cuda.stream(stream):
+        lev[0].record(stream)
+        for i in range(n_dist):
+            layers.replay()
+            lev[i + 1].record(stream)
         sev[0].record(stream)
         for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
+            graphs[i % R].replay()
             sev[i + 1].record(stream)
     torch.cuda.synchronize()
-    per_step_us = np.array([sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(args.steps)])
+    per_step_us = np.array([lev[i].elapsed_time(lev[i + 1]) * 1e3 / R for i in range(n_dist)])
+    per_single_us = np.array([sev[i].elapsed_time(sev[i + 1]) * 1e3 for i in range(args.steps)])
+    del layers
 
     # the pruner and the sparse decode (stages a2-a5) alone, on the selection the step made:
     # one graph of the fused estimate + top-p call and the decode call for every replica in
@@ -676,10 +667,15 @@ def main():
                                f"head_dim={spec.d}, n={spec.n or spec.n_range}, "
                                f"Quest budget={w.budget} pages, p={p}",
                    "config_id": args.config, "p": p, "layer_replicas": len(reps),
-                   "launch": "hipGraph per step"},
+                   "launch": f"hipGraph of {len(reps)} steps, one per layer replica"},
         "step_us_median": float(np.median(per_step_us)),
         "step_us_p90": float(np.percentile(per_step_us, 90)),
-        "step_us_events_mean": float(per_step_us.mean()),
+        "single_step_graph": {
+            "us_per_step": single_graph_ms * 1e3,
+            "us_median": float(np.median(per_single_us)),
+            "us_p90": float(np.percentile(per_single_us, 90)),
+            "note": "one graph launch per step; the difference to us_per_step is graph-launch "
+                    "time between steps, not stage device time"},
         "hbm_frac_step": step_bytes / step_s / HBM_PEAK,
         "step_bytes": step_bytes,
         "pruner_and_decode": {
