@@ -14,23 +14,47 @@ from tests import parity  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-# (config, p, sampled units): units are (sequence, KV head)
+# (config, p); the units checked against the oracle are chosen by sampled_units
 CASES = {
-    "cfg2-longchat-mha-32k": (2, 0.85, [(0, 0), (0, 17)]),
-    "cfg3-llama-gqa-128k": (3, 0.9, [(0, 0), (0, 5)]),
-    "cfg4-longchat-b32-ragged": (4, 0.85, [(3, 7), (30, 21)]),
-    "cfg5-llama-gqa-b8-64k-p0.8": (5, 0.8, [(1, 2)]),
-    "cfg5-llama-gqa-b8-64k-p0.95": (5, 0.95, [(6, 7)]),
+    "cfg2-longchat-mha-32k": (2, 0.85),
+    "cfg3-llama-gqa-128k": (3, 0.9),
+    "cfg4-longchat-b32-ragged": (4, 0.85),
+    "cfg5-llama-gqa-b8-64k-p0.8": (5, 0.8),
+    "cfg5-llama-gqa-b8-64k-p0.9": (5, 0.9),
+    "cfg5-llama-gqa-b8-64k-p0.95": (5, 0.95),
 }
+
+
+def sampled_units(w, n_units=4):
+    """(sequence, KV head) units for the oracle: half with planted heavy keys and half
+    without when the workload has both, spread over the batch (the shortest and the longest
+    sequence among them when lengths differ), seeded."""
+    s = w.spec
+    rng = np.random.default_rng(11 + s.cfg_id)
+    planted = sorted(w.planted)
+    plain = sorted((b, g) for b in range(s.B) for g in range(s.Hkv)
+                   if (b, g) not in w.planted and int(w.seq_lens[b]) > 0)
+    if not planted or not plain:
+        pool = planted or plain
+        lens = np.array([int(w.seq_lens[b]) for b, _ in pool])
+        pick = {int(np.argmin(lens)), int(np.argmax(lens))}
+        rest = [i for i in rng.permutation(len(pool)) if i not in pick]
+        pick.update(int(i) for i in rest[:n_units - len(pick)])
+        return [pool[i] for i in sorted(pick)]
+    half = n_units // 2
+    a = [planted[i] for i in sorted(rng.choice(len(planted), half, replace=False))]
+    c = [plain[i] for i in sorted(rng.choice(len(plain), n_units - half, replace=False))]
+    return a + c
 
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", list(CASES))
 def test_full_size_step(name):
     from adaptive_top_sparse_amd import pipeline
-    cfg, p, units = CASES[name]
+    cfg, p = CASES[name]
     print(f"\n[full size] {name}: generating", flush=True)
     w = workloads.make_workload(cfg)
+    units = sampled_units(w)
     s = w.spec
     G = s.G
     c = pipeline.upload(w)
@@ -45,6 +69,17 @@ def test_full_size_step(name):
     weights = buf.weights.cpu().numpy()
     sel = buf.sel_pages.cpu().numpy() if buf.sel_pages is not None else None
     sel_count = buf.sel_count.cpu().numpy() if buf.sel_count is not None else None
+    # the step as bench.py times it (the fused estimate + top-p call) gives the same kept
+    # sets and outputs, bit for bit, on every unit
+    fused = pipeline.alloc_step(c)
+    pipeline.run_step(c, fused, p)
+    torch.cuda.synchronize()
+    assert np.array_equal(fused.kept_count.cpu().numpy(), kept_count)
+    fk = fused.kept.cpu().numpy()
+    for u in np.ndindex(kept_count.shape):
+        assert np.array_equal(fk[u][:kept_count[u]], kept[u][:kept_count[u]]), u
+    assert np.array_equal(fused.out.cpu().numpy().view(np.uint16), out.view(np.uint16))
+    del fused, fk
     # the sampled units' cache rows (int4 codes, metadata, page bounds), gathered on the GPU
     cache_rows = {}
     for b, g in units:
@@ -89,7 +124,8 @@ def test_full_size_step(name):
                 assert max(by_tok[int(t)] for t in dropped) <= kept_w.min() * (1 + 1e-6)
 
     # stage-by-stage parity on sampled units
-    print(f"[full size] {name}: oracle on {units}", flush=True)
+    print(f"[full size] {name}: oracle on {units} (planted: "
+          f"{[u for u in units if u in w.planted]})", flush=True)
     orc = parity.oracle_units(w, p, units)
     sm = parity.sm_scale_for(s.d)
     for (b, g), res in orc.items():
