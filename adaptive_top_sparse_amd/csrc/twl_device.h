@@ -422,6 +422,9 @@ __device__ __forceinline__ float softmax_inv_sum(float L) { return L > 0.f ? 1.f
 // -inf - -inf arises). The exponential runs on the transcendental unit alone: weights below
 // 2^-126 / sum come out 0 instead of subnormal.
 __device__ __forceinline__ float softmax_weight(float v, float M, float inv_l) {
+  // one rounded product, never contracted into the caller's next add, so that every kernel
+  // that forms this weight gets the same bits whether it stores it or sums it at once
+#pragma clang fp contract(off)
   const float mref = M == -INFINITY ? 0.f : M;
   return exp2_unit(v - mref) * inv_l;
 }
