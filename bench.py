@@ -404,13 +404,14 @@ def cpu_baseline(w, p, seconds, max_threads=16):
     s = w.spec
     sm = float(np.float32(1.0 / math.sqrt(s.d)))
     model, usable = cpu_info()
-    threads = max(1, min(max_threads, usable))
     units = [(b, g) for b in range(s.B) for g in range(s.Hkv)]
     # about one second of single-threaded work per unit sample keeps the default run short
     sample = units
     if len(units) > 64:
         rng = np.random.default_rng(0)
         sample = [units[i] for i in sorted(rng.choice(len(units), 64, replace=False))]
+    # one unit per thread at a time: more threads than units would sit idle
+    threads = max(1, min(max_threads, usable, len(sample)))
     prep = _oracle_unit_prep(w, sample)
 
     def one_step(pool):

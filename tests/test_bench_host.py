@@ -62,3 +62,16 @@ def test_missing_or_unreadable_counter_file_gives_none(fake_tree):
     assert bench.measured_traffic("quest_page_scores", 3, 0.9) is None
     traffic.unlink()
     assert bench.measured_traffic("quest_page_scores", 3, 0.9) is None
+
+
+def test_cpu_baseline_reports_the_threads_that_ran():
+    """The host oracle baseline on the one-unit workload: both variants run, and the
+    multi-threaded one counts only the threads that had a unit to work on."""
+    from adaptive_top_sparse_amd import workloads
+    w = workloads.make_workload(1)
+    r = bench.cpu_baseline(w, 0.9, seconds=0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "candidate tokens/s"
+    assert r["units_per_step"] == 1
+    assert r["cores"] == 1
+    assert r["value"] > 0 and r["single_thread"]["value"] > 0 and r["single_thread"]["cores"] == 1
+    assert r["usable_cores"] >= 1 and r["cpu_model"]
