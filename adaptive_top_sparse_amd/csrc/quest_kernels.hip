@@ -170,9 +170,9 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   constexpr int kBins = 2048;
   constexpr int BPT = kBins / NT;
   constexpr int NW = NT / kWave;
-  // digit histogram, digit d at bucket_slot<NT, BPT>(d); after a pass has picked its digit
+  // digit histogram, digit d at hist[d]; after a pass has picked its digit
   // it doubles as scratch for the short-bucket finish
-  __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ uint32_t scan_lds[NT / kWave + 1];
   __shared__ uint64_t red64[NT / kWave], red64b[NT / kWave];
   __shared__ uint32_t pick[3];
@@ -260,8 +260,7 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         if (first + i < P && (key[i] & mask) == prefix)
-          atomicAdd(&hist[bucket_slot<NT, BPT>(static_cast<uint32_t>((key[i] >> lo_bit) & dmask))],
-                    1u);
+          atomicAdd(&hist[static_cast<uint32_t>((key[i] >> lo_bit) & dmask)], 1u);
       }
       __syncthreads();
       uint32_t above, cnt;

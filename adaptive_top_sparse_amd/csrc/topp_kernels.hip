@@ -54,12 +54,14 @@ struct ToppShape {
 // scaling); its integer part above 2^32 converts exactly, and x minus that part is again
 // exact in fp32 (it keeps at most x's 24 significant bits), so two truncating conversions
 // give floor(x) with no 64-bit shifts.
-__device__ __forceinline__ uint64_t fixed_mass(uint32_t key, int e) {
-  if ((key >> 23) == 0) return 0;
+__device__ __forceinline__ uint64_t fixed_mass_normal(uint32_t key, int e) {
   const float x = ldexpf(__uint_as_float(key), 40 - e);
   const uint32_t hi = static_cast<uint32_t>(x * 0x1p-32f);
   const uint32_t lo = static_cast<uint32_t>(fmaf(-static_cast<float>(hi), 0x1p32f, x));
   return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t fixed_mass(uint32_t key, int e) {
+  return (key >> 23) == 0 ? 0ull : fixed_mass_normal(key, e);
 }
 
 template <int VW>
@@ -206,9 +208,9 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   constexpr int VW = M::VW, NR = M::NR, NL = M::NL;
   constexpr int NW = S::kWaves, BPT = S::kBpt;
   static_assert(NL == 0 || VW == 4, "LDS-resident vectors are four wide");
-  // the mass histogram, bucket b at bucket_slot<NT, BPT>(b); after a pass has picked its
-  // bucket it doubles as scratch for the short-bucket finish
-  __shared__ uint64_t mass[kBins];
+  // the mass histogram, bucket b at mass[b]; after a pass has picked its bucket it doubles
+  // as scratch for the short-bucket finish
+  __shared__ __attribute__((aligned(16))) uint64_t mass[kBins];
   __shared__ f32x4 w_lds[NL > 0 ? NL * NT : 1];
   __shared__ uint32_t red_a[NW], red_b[NW], wave_tot[NW];
   __shared__ uint64_t red64[NW];
@@ -376,10 +378,13 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   } else if (kmax != 0) {
     // fixed-point masses relative to the largest weight's binade
     const int e = static_cast<int>((kmax >> 23) & 0xff) - 127;
-    // the first pass covers every positive W, so its scan yields the total mass and the
-    // target ceil(p * total)
+    // the first pass covers every W of nonzero mass, so its scan yields the total mass and
+    // the target ceil(p * total). Keys below kz (W < 2^(e - 40), subnormals included) have
+    // mass 0 at this resolution: they add nothing and cannot hold tau (the target is at
+    // least 1), so the search range starts at kz and every key inside it has mass >= 1.
+    const uint32_t kz = e + 87 > 0 ? static_cast<uint32_t>(e + 87) << 23 : 0x00800000u;
     uint64_t rem = 0;
-    uint32_t lo = kmin, hi = kmax;
+    uint32_t lo = kmin > kz ? kmin : kz, hi = kmax;
     int pass_no = 0;
     for (;;) {
       const uint32_t range = hi - lo;
@@ -394,10 +399,11 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll
         for (int j = 0; j < VW; ++j) {
+          // k in [lo, hi] as one unsigned comparison of its offset
           const uint32_t k = __float_as_uint(w[j]);
-          if (k >= lo && k <= hi) {
-            const uint64_t m = fixed_mass(k, e);
-            if (m != 0) atomicAdd(&mass[bucket_slot<NT, BPT>((k - lo) >> shift)], m);
+          const uint32_t d = k - lo;
+          if (d <= range) {
+            atomicAdd(&mass[d >> shift], fixed_mass_normal(k, e));
           }
         }
         // keep the scheduler from forming every vector's 64-bit masses ahead of the
@@ -430,11 +436,12 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       // tau is then the largest key whose mass together with every larger key of the
       // bucket reaches rem (0 < rem <= the bucket's mass, so one exists).
       const int par = pass_no & 1;
+      const uint32_t brange = hi - lo;
       for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll
         for (int j = 0; j < VW; ++j) {
           const uint32_t k = __float_as_uint(w[j]);
-          if (k >= lo && k <= hi) {
+          if (k - lo <= brange) {
             const uint32_t idx = atomicAdd(&n_short[par], 1u);
             if (idx < kWave) short_keys[idx] = k;
           }
@@ -477,7 +484,10 @@ __global__ __launch_bounds__(NT) void topp_kernel(
   }
 
   // compaction in slot order: wave totals first, then per-vector wave scans
-  auto kept_w = [&](float w) { return keep_all ? w >= 0.f : (w > 0.f && w >= tau); };
+  // (tau > 0 below p = 1, so W >= tau already excludes W = 0 and the -1 of non-candidates;
+  // with no positive W and p < 1 nothing is kept)
+  const float thr = keep_all ? 0.f : (kmax != 0 ? tau : INFINITY);
+  auto kept_w = [&](float w) { return w >= thr; };
   uint32_t nk = 0;
   for_each_w([&](int, const float(&w)[VW]) {
 #pragma unroll

@@ -333,10 +333,10 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* ld
   return block_excl_scan<NT, uint32_t>(v, lds, total);
 }
 
-// Boundary bucket of a descending selection over NT * BPT buckets kept in LDS. Thread t
-// owns the contiguous buckets [t*BPT, (t+1)*BPT); bucket b is stored at
-// bins[(b % BPT) * NT + b / BPT] (see bucket_slot), so that the owners' reads are
-// conflict-free. Returns the bucket b* with weight(buckets > b*) < rem <= weight(buckets >=
+// Boundary bucket of a descending selection over NT * BPT buckets kept in LDS, bucket b at
+// bins[b] (`bins` aligned to BPT elements). Thread t owns the contiguous buckets
+// [t*BPT, (t+1)*BPT) and reads them in one vector load, so the wave's reads are one
+// contiguous, conflict-free stretch. Returns the bucket b* with weight(buckets > b*) < rem <= weight(buckets >=
 // b*); *above = weight(buckets > b*), *in = weight(b*). `lds` holds NT/64 elements, `pick`
 // 3. Requires 0 < rem <= total weight. When frac > 0, rem is replaced by
 // max(1, ceil(frac * total weight)) and *rem_used receives it, so a first pass needs no
@@ -344,11 +344,6 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* ld
 // before the second barrier and reads `pick` after it, so the caller must pass a block
 // barrier before it writes `pick` or `lds` again (the radix selections here always do, in
 // the passes between two picks).
-template <int NT, int BPT>
-__device__ __forceinline__ int bucket_slot(uint32_t b) {
-  return static_cast<int>((b % BPT) * NT + b / BPT);
-}
-
 template <int NT, int BPT, typename T>
 __device__ __forceinline__ uint32_t block_pick_bucket_lds(const T* bins, T rem, T* lds, T* pick,
                                                           T* above, T* in, float frac = 0.f,
@@ -356,11 +351,13 @@ __device__ __forceinline__ uint32_t block_pick_bucket_lds(const T* bins, T rem, 
   constexpr int NW = NT / kWave;
   const int t = threadIdx.x;
   const int w = t / kWave;
+  typedef T TV __attribute__((ext_vector_type(BPT)));
+  const TV bvv = *reinterpret_cast<const TV*>(bins + t * BPT);
   T bv[BPT];
   T mine = T(0);
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    bv[i] = bins[i * NT + t];
+    bv[i] = bvv[i];
     mine += bv[i];
   }
   const T incl = wave_incl_scan(mine);
