@@ -44,15 +44,17 @@ constexpr int kNormSlots = kNormThreads * 16;  // weights per normalization work
 // Lane (t, c4) scales its group's dot products (scale, plus zero * Q_grp once per real
 // group), the four lane groups' terms are summed across rows, and lane (t, c4) keeps head
 // c4 (and c4 + 4). A dot product is invariant to a common permutation of both operands, so
-// the channel slots are ordered for cheap unpacking: a mask of the same few bits of both
-// 16-bit halves of a code word yields two codes at once. With 4-bit codes a word holds 8
-// channels and instruction pair (2w, 2w+1) takes its slots {0,4,1,5} and {2,6,3,7}; with
-// 2-bit codes a word holds 16 channels and instructions 4w..4w+3 take {0,8,1,9}, {2,10,3,11},
-// {4,12,5,13}, {6,14,7,15}. Every product of an fp16 q and a code is exact in fp32.
+// the channel slots are ordered for cheap unpacking. With 4-bit codes a word holds 8
+// channels; its even and odd nibbles are spread into bytes and converted two at a time
+// (code_pairs_fp8), so instruction pair (2w, 2w+1) takes its slots {0,2,1,3} and
+// {4,6,5,7}. With 2-bit codes a mask of the same bits of both 16-bit halves of a word yields
+// two codes at once; a word holds 16 channels and instructions 4w..4w+3 take {0,8,1,9},
+// {2,10,3,11}, {4,12,5,13}, {6,14,7,15}. Every product of an fp16 q and a code is exact in
+// fp32.
 template <int BITS>
 __device__ __forceinline__ int mfma_channel(int c4, int vg_channels, int m, int e) {
   if constexpr (BITS == 4) {
-    constexpr int kPerm[2][4] = {{0, 4, 1, 5}, {2, 6, 3, 7}};
+    constexpr int kPerm[2][4] = {{0, 2, 1, 3}, {4, 6, 5, 7}};
     return c4 * vg_channels + 8 * (m / 2) + kPerm[m % 2][e];
   } else {
     const int mm = m % 4;
@@ -90,6 +92,22 @@ __device__ __forceinline__ void code_pairs(uint32_t w, uint32_t (&bw)[16 / BITS]
                                            std::integer_sequence<int, K...>) {
   const uint32_t w_hi = w >> 8;
   ((bw[K] = code_pair<BITS, K>(w, w_hi, exp_v)), ...);
+}
+
+// The eight 4-bit codes of a word as four pairs of exact fp16 integers: the even and the
+// odd nibbles are spread into bytes of their own, and a byte holding n in [0, 15] is, read
+// as an fp8 e4m3 number, exactly n * 2^-9 (the subnormals and the first binade of e4m3 are
+// evenly spaced). gfx950 converts two such bytes to fp16 at once, times a power-of-two
+// scale, here 2^9, which makes them n again. Pairs: nibbles {0, 2}, {1, 3}, {4, 6},
+// {5, 7}. 7 instructions per word instead of 9.
+__device__ __forceinline__ void code_pairs_fp8(uint32_t w, uint32_t (&bw)[4]) {
+  constexpr float kScale = 512.f;
+  const uint32_t ev = w & 0x0f0f0f0fu;         // nibbles 0, 2, 4, 6 in bytes 0..3
+  const uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // nibbles 1, 3, 5, 7
+  bw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, kScale, false));
+  bw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, kScale, false));
+  bw[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, kScale, true));
+  bw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, kScale, true));
 }
 
 // *(p + off bytes) with p wave-uniform and off a 32-bit vector offset: the load takes the
@@ -321,7 +339,11 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
         const uint32_t w = cw0[i].w[wi];
         constexpr int kPairs = 16 / BITS;  // code pairs per word
         uint32_t bw[kPairs];
-        code_pairs<BITS>(w, bw, code_exp_v, std::make_integer_sequence<int, kPairs>());
+        if constexpr (BITS == 4) {
+          code_pairs_fp8(w, bw);
+        } else {
+          code_pairs<BITS>(w, bw, code_exp_v, std::make_integer_sequence<int, kPairs>());
+        }
 #pragma unroll
         for (int m = 0; m < kPairs / 2; ++m)
           bq[wi * (kPairs / 2) + m] = __builtin_bit_cast(f16x4, u32x2{bw[2 * m], bw[2 * m + 1]});
@@ -430,11 +452,11 @@ __global__ __launch_bounds__(kNormThreads) void estimate_normalize_kernel(
     const float2 ml = merge_max_sum_wave(partials + hrow * n_chunks, n_chunks);
     if (threadIdx.x == 0) {
       s_ml[0] = ml.x;
-      s_ml[1] = ml.y;
+      s_ml[1] = softmax_inv_sum(ml.y);  // once per row, not per thread
     }
   }
   __syncthreads();
-  const float M = s_ml[0], inv_l = softmax_inv_sum(s_ml[1]);
+  const float M = s_ml[0], inv_l = s_ml[1];
   if (first >= n_slots) return;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

@@ -134,14 +134,14 @@ __global__ __launch_bounds__(kMeanThreads) void topp_mean_kernel(
       const float2 ml = merge_max_sum_wave(norm + (unit * G + h) * norm_chunks, norm_chunks);
       if (lane_id() == 0) {
         s_norm[0][h] = ml.x;
-        s_norm[1][h] = ml.y;
+        s_norm[1][h] = softmax_inv_sum(ml.y);  // once per head, not per thread
       }
     }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       nM[h] = s_norm[0][h];
-      nL[h] = softmax_inv_sum(s_norm[1][h]);
+      nL[h] = s_norm[1][h];
     }
   }
   const int n = seq_len_clamped(seq_lens, b, max_pages);
@@ -266,14 +266,14 @@ __global__ __launch_bounds__(NT) void topp_kernel(
       const float2 ml = merge_max_sum_wave(norm + (unit * G + h) * norm_chunks, norm_chunks);
       if (lane == 0) {
         s_norm[0][h] = ml.x;
-        s_norm[1][h] = ml.y;
+        s_norm[1][h] = softmax_inv_sum(ml.y);  // once per head, not per thread
       }
     }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       nM[h] = s_norm[0][h];
-      nL[h] = softmax_inv_sum(s_norm[1][h]);
+      nL[h] = s_norm[1][h];
     }
   };
   // a batch of NB vectors: all loads (weights and page ids) first, then W
