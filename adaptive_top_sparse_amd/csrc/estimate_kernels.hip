@@ -197,14 +197,15 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
   // batch's entries does not also wait for the ids already requested for the batch after
   // next, as a wait on a scalar load would, and the pipeline below stays three deep.
   // Once such a value has arrived it is made scalar (readfirstlane), so that the checks and
-  // address arithmetic that follow run on the scalar unit.
+  // address arithmetic that follow run on the scalar unit. The loaded word is kept as it
+  // came; the rank replaces it only where it is used (load_phys), since a select right after
+  // the load would make the wave wait for it there, two batches early.
   const int32_t* id_src = crow != nullptr ? crow : page_table;
   auto load_ids = [&](int j, int (&pid)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int r = rank_of(j, i);
-      const int v = load_at(id_src + (crow != nullptr ? (r < page_end ? r : page0) : 0), 0u);
-      pid[i] = crow == nullptr ? r : v;
+      pid[i] = load_at(id_src + (crow != nullptr ? (r < page_end ? r : page0) : 0), 0u);
     }
   };
   int ids0[PB], ids1[PB];
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int r = rank_of(j, i);
-      const int ps = __builtin_amdgcn_readfirstlane(pid[i]);
+      const int ps = crow == nullptr ? r : __builtin_amdgcn_readfirstlane(pid[i]);
       const bool ok = (r < page_end) & (r < cnt) & (ps >= 0) & (ps < max_pages) &
                       (ps * kPage < n);
       pid[i] = ok ? ps : -1;
@@ -310,7 +311,6 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
 #pragma unroll
   for (int i = 0; i < PB; ++i) keep_loaded(phys0[i]);
   load_codes(ids0, phys0, cw0, mw0);
-  if (n_batches > 1) load_phys(1, ids1, phys1);
 
   uint32_t code_exp_v[5];  // code_exp(2i), held in VGPRs (vz is an opaque zero)
   const int vz = vgpr_zero();
@@ -322,13 +322,9 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     run_m[hb] = -INFINITY;
     run_l[hb] = 0.f;
   }
-  for (int j = 0; j < n_batches; ++j) {
-    int ids2[PB];
-    if (j + 2 < n_batches) load_ids(j + 2, ids2);
-    CodeWords<NW> cw1[PB];
-    uint32_t mw1[PB];
-    if (j + 1 < n_batches) load_codes(ids1, phys1, cw1, mw1);
-
+  // Batch j: the tiles of its pages (codes in cw0, {scale, zero} in mw0, ids in ids0), their
+  // logits written and folded into the online (max, sum of exp).
+  auto batch = [&](int j) {
     float s[PB][NHB];
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
@@ -392,22 +388,45 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
         run_m[hb] = mn;
       }
     }
-    // rotate the pipeline: batch j + 1 (codes in flight) becomes current, then batch j + 2
-    // (page ids in hand) gets its page-table entries
-    if (j + 1 < n_batches) {
+  };
+  // Pipeline: page ids two batches ahead, page-table entries and codes one ahead. The
+  // steady-state loop runs while batch j + 2 exists, so that it issues the same loads on
+  // every path: the compiler's wait before a batch's codes then covers the page-table
+  // entries alone. (Issuing the loads only while needed, inside the loop, made it wait for
+  // the page ids just requested, a round trip per batch.) The last two batches are peeled.
+  if (n_batches >= 2) {
+    load_phys(1, ids1, phys1);
+    for (int j = 0; j + 2 < n_batches; ++j) {
+      int ids2[PB];
+      load_ids(j + 2, ids2);
+      CodeWords<NW> cw1[PB];
+      uint32_t mw1[PB];
+      load_codes(ids1, phys1, cw1, mw1);
+      batch(j);
+      // rotate: batch j + 1 (codes in flight) becomes current, then batch j + 2 (page ids
+      // in hand) gets its page-table entries
 #pragma unroll
       for (int i = 0; i < PB; ++i) {
         ids0[i] = ids1[i];
         cw0[i] = cw1[i];
         mw0[i] = mw1[i];
       }
-    }
-    if (j + 2 < n_batches) {
       load_phys(j + 2, ids2, phys1);
 #pragma unroll
       for (int i = 0; i < PB; ++i) ids1[i] = ids2[i];
     }
+    CodeWords<NW> cw1[PB];
+    uint32_t mw1[PB];
+    load_codes(ids1, phys1, cw1, mw1);
+    batch(n_batches - 2);
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      ids0[i] = ids1[i];
+      cw0[i] = cw1[i];
+      mw0[i] = mw1[i];
+    }
   }
+  batch(n_batches - 1);
   // (max, sum exp) per head: over the row's 16 tokens, then over the waves
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
