@@ -243,20 +243,10 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
   bool live0[U];
   u32x4 kx0[KX], vv0[U];
   load_kv(phys0, tok0, live0, kx0, vv0);
-  if constexpr (!kSingle) {
-    if (n_batches > 1) load_rows(1, t1, ids1, phys1, tok1);
-  }
 
-  for (int j = 0; j < n_batches; ++j) {
-    // ids of batch j + 2 and K/V of batch j + 1 go out before batch j is used
-    int ids2[NU];
-    bool live1[U];
-    u32x4 kx1[KX], vv1[U];
-    if constexpr (!kSingle) {
-      if (j + 2 < n_batches) load_ids(j + 2, ids2);
-      if (j + 1 < n_batches) load_kv(phys1, tok1, live1, kx1, vv1);
-    }
-
+  // batch j: scores of the lane's rows (K in kx0), their weights and the running softmax
+  // state, and p.v into acc (V in vv0)
+  auto batch = [&](int j) {
     // weights pr[u][h] of the lane's V rows and the rescale alpha[h] of the old state.
     // Exponentials are taken against the new max, or against 0 while a head has no live
     // token yet, which gives exactly 0 for -inf scores and a -inf old max.
@@ -349,9 +339,24 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
         for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(pr[u][h], vf[c], acc[h][c]);
       }
     }
-    // rotate the pipeline
-    if constexpr (!kSingle) {
-      if (j + 2 < n_batches) {
+  };
+  if constexpr (kSingle) {
+    batch(0);
+  } else {
+    // The pipeline (ids two batches ahead, page entries and K/V one ahead) runs its
+    // steady state while batch j + 2 exists, issuing the same loads on every path: the
+    // compiler's wait before a batch's K/V then covers its page entries alone. (Loads issued
+    // only while needed, inside one loop, made it wait for the ids just requested, a round
+    // trip per batch.) The last two batches are peeled.
+    if (n_batches > 1) {
+      load_rows(1, t1, ids1, phys1, tok1);
+      for (int j = 0; j + 2 < n_batches; ++j) {
+        int ids2[NU];
+        bool live1[U];
+        u32x4 kx1[KX], vv1[U];
+        load_ids(j + 2, ids2);
+        load_kv(phys1, tok1, live1, kx1, vv1);
+        batch(j);
         int phys2[NU], tok2[NU];
         load_rows(j + 2, t1, ids2, phys2, tok2);
 #pragma unroll
@@ -359,7 +364,18 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
           phys1[u] = phys2[u];
           tok1[u] = tok2[u];
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          live0[u] = live1[u];
+          vv0[u] = vv1[u];
+        }
+#pragma unroll
+        for (int u = 0; u < KX; ++u) kx0[u] = kx1[u];
       }
+      bool live1[U];
+      u32x4 kx1[KX], vv1[U];
+      load_kv(phys1, tok1, live1, kx1, vv1);
+      batch(n_batches - 2);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         live0[u] = live1[u];
@@ -368,6 +384,7 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
 #pragma unroll
       for (int u = 0; u < KX; ++u) kx0[u] = kx1[u];
     }
+    batch(n_batches - 1);
   }
   if constexpr (kMfma) {
 #pragma unroll
