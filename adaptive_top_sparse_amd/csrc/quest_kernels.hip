@@ -413,6 +413,15 @@ hipError_t launch_quest_scores(const Layout& L, const void* q, const void* minma
 
 hipError_t launch_quest_top(const Layout& L, const double* scores, int budget,
                             int32_t* sel_pages, int32_t* sel_count, hipStream_t s) {
+  // up to 2048 pages per sequence: 512-thread blocks, four to a CU, so a large batch of
+  // units selects in one round (13.5 -> 10.4 us on the B = 32 ragged MHA step)
+  if (L.max_pages <= 2048) {
+    const int k5 = (L.max_pages + 511) / 512;
+    if (k5 <= 1) select_launch<512, 1>(L, budget, sel_pages, sel_count, scores, s);
+    else if (k5 <= 2) select_launch<512, 2>(L, budget, sel_pages, sel_count, scores, s);
+    else select_launch<512, 4>(L, budget, sel_pages, sel_count, scores, s);
+    return hipGetLastError();
+  }
   const int kpt = (L.max_pages + 1023) / 1024;
   if (kpt <= 1) select_launch<1024, 1>(L, budget, sel_pages, sel_count, scores, s);
   else if (kpt <= 2) select_launch<1024, 2>(L, budget, sel_pages, sel_count, scores, s);
