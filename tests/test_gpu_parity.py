@@ -28,6 +28,10 @@ CASES = {
     # units above 32768 slots keep half of W in LDS: GQA (wide pass) and MHA (direct)
     "cfg5-n40k": (5, dict(B=1, n=40000 + 3), 0.9),
     "cfg5-n40k-mha": (5, dict(B=1, n=40000 + 3, Hq=4, Hkv=4), 0.9),
+    # long enough that the estimate takes 64-page chunks (four batches per wave: the
+    # steady-state loop, then the two peeled batches; the ragged last chunk three) and the
+    # decode 512-token chunks (up to eight batches each)
+    "cfg5-b2-n40k": (5, dict(B=2, n=2536 * 16 - 5), 0.9),
     # the 2-bit key cache of the pages' ablation: every head dim, group size and selector
     "cfg1-2bit": (1, {}, 0.9, 2),
     "cfg3s-2bit": (3, dict(n=8192 + 5, budget=64), 0.9, 2),
