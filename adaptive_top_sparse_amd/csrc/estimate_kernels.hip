@@ -62,8 +62,9 @@ __device__ __forceinline__ int mfma_channel(int c4, int vg_channels, int m, int 
   }
 }
 
-// Codes K of both 16-bit halves of a code word (bits [p + BITS - 1 : p] of each half,
-// p = BITS * K) as two exact fp16 integers. A field that lies inside the fp16 significand
+// (2-bit codes; 4-bit codes go through code_pairs_fp8 below.) Codes K of both 16-bit
+// halves of a code word (bits [p + BITS - 1 : p] of each half, p = BITS * K) as two exact
+// fp16 integers. A field that lies inside the fp16 significand
 // (p + BITS <= 10) is converted where it stands: with the exponent of 2^(10 - p) or-ed in,
 // the half reads 2^(10 - p) + n exactly (its ulp is 1 there), and subtracting 2^(10 - p)
 // leaves n. Higher fields are first shifted down by 8 bits, one shift that serves all of

@@ -2,7 +2,8 @@
 // pages, atlas.scime.ai summary: "Approach" for top-p thresholding of the estimated weights
 // with binary-search top-p kernels, "Limitations" for the group-wise budget under GQA).
 //
-// The search for tau runs on chip, one 1024-thread block per (sequence, KV head):
+// The search for tau runs on chip, one block per (sequence, KV head) (1024 threads; 512 for
+// units of up to 4096 slots):
 //  * W_j = mean over the group's heads of the weights (fp32, fixed head order).
 //  * Masses are exact integers: M_j = floor(W_j * 2^(40 - e)), e the binary exponent of the
 //    unit's largest W, so every sum is independent of order and the result is
@@ -10,13 +11,15 @@
 //  * tau is the largest fp32 value with sum_{W_j >= tau} M_j >= ceil(p * sum_j M_j). The
 //    search narrows the range of fp32 bit patterns (monotone for W >= 0) with 2048-bucket
 //    mass histograms, instead of halving it once per pass: a 31-bit range closes in at
-//    most three passes. As soon as the boundary bucket holds at most 64 weights, they are
-//    gathered and one wave finishes the search over them directly.
+//    most three passes. The range starts at the smallest key of nonzero mass (lighter
+//    weights add nothing and cannot hold tau), so a pass tests each key with one unsigned
+//    comparison and adds its mass with one LDS atomic. As soon as the boundary bucket
+//    holds at most 64 weights, they are gathered and one wave finishes the search.
 //  * W is read from memory once and stays resident for every pass: up to 32 values per
 //    lane in VGPRs, the rest (units above 32768 slots) in LDS.
-//  * Kept = {W_j >= tau, W_j > 0}, compacted in slot order (per-wave scans, then one
+//  * Kept = {W_j >= tau} (tau > 0), compacted in slot order (per-wave scans, then one
 //    exchange of wave totals), which is ascending token order because candidate pages are
-//    ascending.
+//    ascending. p = 1 keeps every valid slot, whatever its W.
 // When the group is large relative to the unit (G * slots-per-thread above what one
 // block's registers take, 128 or 32), a wide
 // pass first forms W over many work-groups into the workspace, so that the per-unit block
@@ -36,15 +39,14 @@ constexpr int kMeanThreads = 256;
 constexpr int kMeanSlots = kMeanThreads * 16;  // slots per work-group of the group-mean pass
 
 // Per block size: W vectors per lane held in VGPRs (the rest live in LDS) and the largest
-// G * slots-per-thread read straight from the weights. A 256-thread block has one wave per
-// SIMD and up to 512 VGPRs per lane, so it keeps a whole 8192-slot unit in registers and
-// issues all of its loads at once; a 1024-thread block has 128.
+// G * slots-per-thread read straight from the weights (a 1024-thread block has 128 VGPRs
+// per lane, a 512-thread block, with units of at most 4096 slots, needs no more).
 template <int NT>
 struct ToppShape {
   static constexpr int kWaves = NT / kWave;
   static constexpr int kRegVecs = 8;
-  static constexpr int kDirectLoads = NT == 256 ? 128 : 32;
-  static constexpr int kRegBatch = NT == 256 ? 8 : 4;  // vectors whose loads go out together
+  static constexpr int kDirectLoads = 32;
+  static constexpr int kRegBatch = 4;  // vectors whose loads go out together
   static constexpr int kBpt = kBins / NT;              // histogram buckets per thread
 };
 
