@@ -35,14 +35,21 @@ namespace {
 #define TWL_DEC_UNROLL 4
 #endif
 #ifndef TWL_DEC_TARGET_BLOCKS
-#define TWL_DEC_TARGET_BLOCKS 2048
+#define TWL_DEC_TARGET_BLOCKS 512
 #endif
 #ifndef TWL_DEC_MAX_BATCHES
 #define TWL_DEC_MAX_BATCHES 16
 #endif
-// A full-length kept list still splits into at least this many chunks.
+// A full-length kept list still splits into at least this many chunks, or, in a step of
+// at most TWL_DEC_FEW_UNITS (sequence, KV head) units, TWL_DEC_MIN_CHUNKS_FEW.
 #ifndef TWL_DEC_MIN_CHUNKS
 #define TWL_DEC_MIN_CHUNKS 16
+#endif
+#ifndef TWL_DEC_MIN_CHUNKS_FEW
+#define TWL_DEC_MIN_CHUNKS_FEW 64
+#endif
+#ifndef TWL_DEC_FEW_UNITS
+#define TWL_DEC_FEW_UNITS 64
 #endif
 constexpr int kDecThreads = TWL_DEC_THREADS;
 constexpr int kDecWaves = kDecThreads / kWave;
@@ -543,16 +550,19 @@ void decode_dispatch_g(const Layout& L, const void* q, const void* k, const void
 int decode_chunk_tokens(const Layout& L, int kept_stride) {
   // about TWL_DEC_TARGET_BLOCKS work-groups over the largest possible kept lists: one to
   // TWL_DEC_MAX_BATCHES batches per work-group, but a full-length list still in at least
-  // TWL_DEC_MIN_CHUNKS chunks, so that lists only partly full (short sequences, strong
-  // pruning) keep several work-groups each. Long lists then take long chunks: fewer
-  // partials to write and merge.
+  // TWL_DEC_MIN_CHUNKS chunks (TWL_DEC_MIN_CHUNKS_FEW when the step has few units), so that
+  // lists only partly full (short sequences, strong pruning) keep several work-groups each.
+  // Long lists then take long chunks: fewer partials to write and merge. (Measured: the
+  // 128k GQA step's 8 units take 128-token chunks, 1.2 us faster than 64; the 32k MHA
+  // step's 32 units keep 64-token chunks, 0.4 us faster than 128.)
   const long units = static_cast<long>(L.B) * L.units();
   const long want =
       (static_cast<long>(kept_stride) * units + TWL_DEC_TARGET_BLOCKS - 1) / TWL_DEC_TARGET_BLOCKS;
+  const long min_chunks = units <= TWL_DEC_FEW_UNITS ? TWL_DEC_MIN_CHUNKS_FEW : TWL_DEC_MIN_CHUNKS;
   const int batch = decode_batch_tokens(L.d);
   long c = batch;
   while (c < want && c < static_cast<long>(batch) * TWL_DEC_MAX_BATCHES &&
-         2 * c * TWL_DEC_MIN_CHUNKS <= kept_stride)
+         2 * c * min_chunks <= kept_stride)
     c <<= 1;
   return static_cast<int>(c);
 }
