@@ -331,37 +331,45 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
     }
   }
 
-  // pages strictly above the boundary prefix are in; of the pages equal to it, the first
-  // `rem` in page order are in (all of them unless exact ties remain)
+  // Pages strictly above the boundary prefix are in; of the pages equal to it, the first
+  // `rem` in page order are in (all of them unless exact ties remain). When all of them
+  // are in, that is key >= prefix (the bits below the mask are free), one pair test.
+  if (mode == kAllIn) {
+    mode = kPair;
+    t_key = prefix;
+    t_page = P;
+  }
   uint32_t tot;
-  uint32_t eq_before = 0;
-  if (mode == kTies) {
+  bool chosen[KPT];
+  uint32_t n_sel = 0;
+  if (mode == kPair) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int pg = first + i;
+      chosen[i] = (pg < P) & ((key[i] > t_key) | ((key[i] == t_key) & (pg <= t_page)));
+      n_sel += chosen[i] ? 1u : 0u;
+    }
+  } else {
     uint32_t n_eq = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
       n_eq += (first + i < P && (key[i] & mask) == prefix) ? 1u : 0u;
-    eq_before = block_excl_scan_u32<NT>(n_eq, scan_lds, &tot);
-  }
-  bool chosen[KPT];
-  uint32_t n_sel = 0;
+    uint32_t eq_before = block_excl_scan_u32<NT>(n_eq, scan_lds, &tot);
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    bool c = false;
-    if (first + i < P) {
-      if (mode == kPair) {
-        c = key[i] > t_key || (key[i] == t_key && first + i <= t_page);
-      } else {
+    for (int i = 0; i < KPT; ++i) {
+      bool c = false;
+      if (first + i < P) {
         const uint64_t km = key[i] & mask;
         if (km > prefix) {
           c = true;
         } else if (km == prefix) {
-          c = mode == kAllIn || eq_before < rem;
+          c = eq_before < rem;
           ++eq_before;
         }
       }
+      chosen[i] = c;
+      n_sel += c ? 1u : 0u;
     }
-    chosen[i] = c;
-    n_sel += c ? 1u : 0u;
   }
   uint32_t pos = block_excl_scan_u32<NT>(n_sel, scan_lds, &tot);
 #pragma unroll

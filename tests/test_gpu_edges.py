@@ -131,6 +131,41 @@ def test_exact_quest_ties_break_by_page_index():
         _check_all(w2, _step(pl, c, buf, 0.85, budget == 3), 0.85)
 
 
+def test_quest_boundary_inside_a_large_group_of_ties():
+    """The top-budget boundary inside 200 pages of one exact score (more ties than one wave
+    ranks), at the group's end, at its start and past it. Keys scaled by powers of two
+    separate three score groups exactly: 50 pages x4, 200 copies of one unscaled page, the
+    rest x1/8."""
+    pl = _pipeline()
+    print("\n[edge] Quest boundary in a large tie group", flush=True)
+    P = 450
+    w = workloads.make_workload(2, n=P * 16, budget=8, Hq=2, Hkv=2)
+    tied = [p for p in range(50, P) if p % 2 == 1][:200]
+    for g in range(2):
+        k = w.k[0][g]
+        src = k[50 * 16:51 * 16].copy()                 # page 50, unscaled (not in `tied`)
+        for p in range(P):
+            rows = slice(p * 16, (p + 1) * 16)
+            if p < 50:
+                k[rows] = k[rows] * np.float16(4)
+            elif p in tied:
+                k[rows] = src
+            else:
+                k[rows] = k[rows] * np.float16(0.125)
+    c = pl.upload(w)
+    c.build_caches()
+    for i, budget in enumerate((80, 250, 50, 257)):
+        c.budget = budget
+        buf = pl.alloc_step(c)
+        w2 = workloads.Workload(**{**vars(w), "budget": budget})
+        orc = _check_all(w2, _step(pl, c, buf, 0.85, i % 2 == 1), 0.85)
+        sel = orc[(0, 0)]["sel"]
+        if budget == 80:                                # the first 30 ties in page order
+            assert np.array_equal(sel, np.array(list(range(50)) + tied[:30]))
+        if budget == 250:
+            assert np.array_equal(sel, np.array(sorted(list(range(50)) + tied)))
+
+
 def test_graph_replay_matches_eager():
     pl = _pipeline()
     print("\n[edge] graph replay", flush=True)
