@@ -49,18 +49,28 @@ def unpack_codes(packed: np.ndarray, bits: int = 4) -> np.ndarray:
     return np.stack(fields, axis=-1).reshape(packed.shape[0], -1)
 
 
-def oracle_units(w, p: float, units=None, headwise: bool = False, key_bits: int = 4):
-    """Oracle results per (b, kvh) unit (all units, or the listed ones)."""
+def oracle_units(w, p: float, units=None, headwise: bool = False, key_bits: int = 4,
+                 threads: int = 1):
+    """Oracle results per (b, kvh) unit (all units, or the listed ones). With threads > 1
+    the units run concurrently (the oracle's C calls release the interpreter lock); each
+    unit's result is the same either way."""
     s = w.spec
     G = s.G
     sm = sm_scale_for(s.d)
     if units is None:
         units = [(b, g) for b in range(s.B) for g in range(s.Hkv)]
-    res = {}
-    for b, g in units:
-        res[(b, g)] = oracle.run_unit(w.q[b, g * G:(g + 1) * G], w.k[b][g], w.v[b][g],
-                                      w.budget, p, sm, headwise=headwise, key_bits=key_bits)
-    return res
+
+    def one(u):
+        b, g = u
+        return oracle.run_unit(w.q[b, g * G:(g + 1) * G], w.k[b][g], w.v[b][g], w.budget, p,
+                               sm, headwise=headwise, key_bits=key_bits)
+
+    if threads > 1 and len(units) > 1:
+        import concurrent.futures
+        oracle.lib()  # loaded (and built if need be) once, before the workers start
+        with concurrent.futures.ThreadPoolExecutor(min(threads, len(units))) as ex:
+            return dict(zip(units, ex.map(one, units)))
+    return {u: one(u) for u in units}
 
 
 def head_view(res, h: int):

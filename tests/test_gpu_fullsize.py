@@ -1,9 +1,12 @@
 """GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
 
-The whole step runs on the GPU for every (sequence, KV head) unit; sampled units are checked
-stage by stage against the oracle (which finishes one unit in seconds), and every unit is
-checked against properties that hold at any size.
+The whole step runs on the GPU for every (sequence, KV head) unit, and every unit is
+checked stage by stage against the oracle (one unit per host thread; a unit takes the
+oracle from a tenth of a second to a few seconds) and against properties that hold at any
+size.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -14,7 +17,7 @@ from tests import parity  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-# (config, p); the units checked against the oracle are chosen by sampled_units
+# (config, p)
 CASES = {
     "cfg2-longchat-mha-32k": (2, 0.85),
     "cfg3-llama-gqa-128k": (3, 0.9),
@@ -24,27 +27,10 @@ CASES = {
     "cfg5-llama-gqa-b8-64k-p0.95": (5, 0.95),
 }
 
-
-def sampled_units(w, n_units=4):
-    """(sequence, KV head) units for the oracle: half with planted heavy keys and half
-    without when the workload has both, spread over the batch (the shortest and the longest
-    sequence among them when lengths differ), seeded."""
-    s = w.spec
-    rng = np.random.default_rng(11 + s.cfg_id)
-    planted = sorted(w.planted)
-    plain = sorted((b, g) for b in range(s.B) for g in range(s.Hkv)
-                   if (b, g) not in w.planted and int(w.seq_lens[b]) > 0)
-    if not planted or not plain:
-        pool = planted or plain
-        lens = np.array([int(w.seq_lens[b]) for b, _ in pool])
-        pick = {int(np.argmin(lens)), int(np.argmax(lens))}
-        rest = [i for i in rng.permutation(len(pool)) if i not in pick]
-        pick.update(int(i) for i in rest[:n_units - len(pick)])
-        return [pool[i] for i in sorted(pick)]
-    half = n_units // 2
-    a = [planted[i] for i in sorted(rng.choice(len(planted), half, replace=False))]
-    c = [plain[i] for i in sorted(rng.choice(len(plain), n_units - half, replace=False))]
-    return a + c
+# oracle worker threads (at most the 16 host cores that go with one GPU), and units per
+# batch of oracle results held at once
+ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
+ORACLE_BATCH = 64
 
 
 @pytest.mark.timeout(600)
@@ -54,8 +40,8 @@ def test_full_size_step(name):
     cfg, p = CASES[name]
     print(f"\n[full size] {name}: generating", flush=True)
     w = workloads.make_workload(cfg)
-    units = sampled_units(w)
     s = w.spec
+    units = [(b, g) for b in range(s.B) for g in range(s.Hkv)]
     G = s.G
     c = pipeline.upload(w)
     c.build_caches()
@@ -80,15 +66,10 @@ def test_full_size_step(name):
         assert np.array_equal(fk[u][:kept_count[u]], kept[u][:kept_count[u]]), u
     assert np.array_equal(fused.out.cpu().numpy().view(np.uint16), out.view(np.uint16))
     del fused, fk
-    # the sampled units' cache rows (int4 codes, metadata, page bounds), gathered on the GPU
-    cache_rows = {}
-    for b, g in units:
-        n = int(w.seq_lens[b])
-        pages = torch.from_numpy(w.page_table[b, :-(-n // 16)].astype(np.int64)).cuda()
-        cache_rows[(b, g)] = (
-            c.k_codes[pages, g].cpu().numpy().reshape(-1, s.d // 2)[:n],
-            c.k_meta[pages, g].cpu().numpy().reshape(-1, s.d // 32, 2)[:n],
-            None if c.page_minmax is None else c.page_minmax[b, g, :pages.numel()].cpu().numpy())
+    # the caches the GPU built (int4 codes, metadata, page bounds), read back whole
+    codes_h = c.k_codes.cpu().numpy()
+    meta_h = c.k_meta.cpu().numpy()
+    mm_h = None if c.page_minmax is None else c.page_minmax.cpu().numpy()
     del c, buf
     torch.cuda.empty_cache()
 
@@ -123,26 +104,36 @@ def test_full_size_step(name):
             if dropped.size and kept_w.size:
                 assert max(by_tok[int(t)] for t in dropped) <= kept_w.min() * (1 + 1e-6)
 
-    # stage-by-stage parity on sampled units
-    print(f"[full size] {name}: oracle on {units} (planted: "
-          f"{[u for u in units if u in w.planted]})", flush=True)
-    orc = parity.oracle_units(w, p, units)
+    # stage-by-stage parity on every unit, in batches of oracle results
+    print(f"[full size] {name}: oracle on all {len(units)} units ({len(w.planted)} planted), "
+          f"{ORACLE_THREADS} threads", flush=True)
     sm = parity.sm_scale_for(s.d)
-    for (b, g), res in orc.items():
-        n = int(w.seq_lens[b])
-        codes, meta, mm = cache_rows[(b, g)]
-        assert np.array_equal(parity.unpack_codes(codes), res["codes"]), (b, g)
-        assert np.array_equal(meta[..., 0].astype(np.float64), res["scale"].astype(np.float64))
-        assert np.array_equal(meta[..., 1].astype(np.float64), res["zero"].astype(np.float64))
-        if mm is not None:
-            assert np.array_equal(mm[:, 0].astype(np.float64), res["lo"].astype(np.float64))
-            assert np.array_equal(mm[:, 1].astype(np.float64), res["hi"].astype(np.float64))
-        if sel is not None:
-            m = int(sel_count[b, g])
-            assert np.array_equal(sel[b, g, :m], res["sel"]), (b, g)
-        parity.check_weights(weights[b, g * G:(g + 1) * G], res["weights"], res["valid"])
-        k = kept[b, g, :kept_count[b, g]]
-        parity.check_kept(k, res, p, n)
-        parity.check_out(out[b, g * G:(g + 1) * G], w.q[b, g * G:(g + 1) * G], w.k[b][g],
-                         w.v[b][g], k, res, sm)
+    for i0 in range(0, len(units), ORACLE_BATCH):
+        orc = parity.oracle_units(w, p, units[i0:i0 + ORACLE_BATCH], threads=ORACLE_THREADS)
+        for (b, g), res in orc.items():
+            n = int(w.seq_lens[b])
+            codes = parity.logical_rows(codes_h, w.page_table[b], n, g)
+            meta = parity.logical_rows(meta_h, w.page_table[b], n, g)
+            assert np.array_equal(parity.unpack_codes(codes), res["codes"]), (b, g)
+            assert np.array_equal(meta[..., 0].astype(np.float64),
+                                  res["scale"].astype(np.float64)), (b, g)
+            assert np.array_equal(meta[..., 1].astype(np.float64),
+                                  res["zero"].astype(np.float64)), (b, g)
+            if mm_h is not None:
+                mm = mm_h[b, g, :-(-n // 16)]
+                assert np.array_equal(mm[:, 0].astype(np.float64),
+                                      res["lo"].astype(np.float64)), (b, g)
+                assert np.array_equal(mm[:, 1].astype(np.float64),
+                                      res["hi"].astype(np.float64)), (b, g)
+            if sel is not None:
+                m = int(sel_count[b, g])
+                assert np.array_equal(sel[b, g, :m], res["sel"]), (b, g)
+            parity.check_weights(weights[b, g * G:(g + 1) * G], res["weights"], res["valid"])
+            k = kept[b, g, :kept_count[b, g]]
+            parity.check_kept(k, res, p, n)
+            parity.check_out(out[b, g * G:(g + 1) * G], w.q[b, g * G:(g + 1) * G], w.k[b][g],
+                             w.v[b][g], k, res, sm)
+        del orc
+        print(f"[full size] {name}: {min(i0 + ORACLE_BATCH, len(units))} units match",
+              flush=True)
     print(f"[full size] {name}: ok, kept {int(kept_count.sum())} token-heads", flush=True)
