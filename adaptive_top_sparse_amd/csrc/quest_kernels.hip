@@ -215,16 +215,18 @@ __global__ __launch_bounds__(NT) void quest_select_kernel(
   // orders these stores before its atomics
 #pragma unroll
   for (int i = 0; i < BPT; ++i) hist[i * NT + threadIdx.x] = 0;
+  // pages past the sequence get key 0, below every score's key, so they never raise kmax
+  // (selects rather than branches: the loop stays straight-line code)
   uint64_t key[KPT];
   uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int p = first + i;
-    key[i] = p < P ? f64_order_key(sv[i]) : 0ull;
-    if (p < P) {
-      kmin = key[i] < kmin ? key[i] : kmin;
-      kmax = key[i] > kmax ? key[i] : kmax;
-    }
+    const bool ok = first + i < P;
+    const uint64_t k = f64_order_key(sv[i]);
+    key[i] = ok ? k : 0ull;
+    const uint64_t kl = ok ? k : ~0ull;
+    kmin = kl < kmin ? kl : kmin;
+    kmax = key[i] > kmax ? key[i] : kmax;
   }
   block_minmax<NT, uint64_t>(kmin, kmax, red64, red64b, ~0ull, 0ull, &kmin, &kmax);
 
