@@ -454,8 +454,9 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
 }
 
 // Merge of the chunk partials when they are more than one: one wave per (sequence, query
-// head, 32-channel slice: a whole 128-byte line of each chunk's record). Lane i takes chunks i, i + 64, ... with a running (max, sum, o)
-// of its own; the lanes are then combined on the common maximum. The (max, sum) pairs sit
+// head, 32-channel slice: a whole 128-byte line of each chunk's record). Lane i takes
+// chunks i, i + 64, ... with a running (max, sum, o) of its own; the lanes are then
+// combined on the common maximum. The (max, sum) pairs sit
 // in their own compact array and each chunk's o in a 512-byte record, so every byte of the
 // partials is fetched once.
 template <int D>

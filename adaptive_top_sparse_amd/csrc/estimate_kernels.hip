@@ -8,8 +8,9 @@
 //   s_hj = sm_scale * sum_groups [zero * Q_grp,h + scale * sum_{c in grp} q_hc * code_c],
 // with Q_grp,h = sum_{c in grp} q_hc, the same value as q_h . dequant(k_j). Then a softmax
 // over the unit's valid candidates, done as per-chunk (max, sum of exp) partials followed
-// by a normalization pass. The logits are kept in log2 units (s_hj * log2 e), so that every
-// exponential is one exp2.
+// by a normalization pass (or, in the fused estimate + top-p call, normalised by the top-p
+// kernel as it reads the logits). The logits are kept in log2 units (s_hj * log2 e), so
+// that every exponential is one exp2.
 #include <utility>
 
 #include "twl_device.h"
@@ -448,7 +449,8 @@ __global__ __launch_bounds__(kEstChunk) void estimate_logits_kernel(
     for (int w2 = 1; w2 < kEstWaves; ++w2) M = fmaxf(M, red_m[w2][h]);
     float L = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kEstWaves; ++w2) L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * exp2_unit(red_m[w2][h] - M) : 0.f;
+    for (int w2 = 0; w2 < kEstWaves; ++w2)
+      L += red_m[w2][h] > -INFINITY ? red_l[w2][h] * exp2_unit(red_m[w2][h] - M) : 0.f;
     partials[(static_cast<long>(b) * Hq + g * G + h) * n_chunks + chunk] = make_float2(M, L);
   }
 }

@@ -20,10 +20,9 @@
 //  * Kept = {W_j >= tau} (tau > 0), compacted in slot order (per-wave scans, then one
 //    exchange of wave totals), which is ascending token order because candidate pages are
 //    ascending. p = 1 keeps every valid slot, whatever its W.
-// When the group is large relative to the unit (G * slots-per-thread above what one
-// block's registers take, 128 or 32), a wide
-// pass first forms W over many work-groups into the workspace, so that the per-unit block
-// does not stream G rows of weights through one CU.
+// When the group is large relative to the unit (G * slots-per-thread above 32, what one
+// block's registers take), a wide pass first forms W over many work-groups into the
+// workspace, so that the per-unit block does not stream G rows of weights through one CU.
 #include <type_traits>
 
 #include "twl_device.h"

@@ -336,9 +336,10 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* ld
 // Boundary bucket of a descending selection over NT * BPT buckets kept in LDS, bucket b at
 // bins[b] (`bins` aligned to BPT elements). Thread t owns the contiguous buckets
 // [t*BPT, (t+1)*BPT) and reads them in one vector load, so the wave's reads are one
-// contiguous, conflict-free stretch. Returns the bucket b* with weight(buckets > b*) < rem <= weight(buckets >=
-// b*); *above = weight(buckets > b*), *in = weight(b*). `lds` holds NT/64 elements, `pick`
-// 3. Requires 0 < rem <= total weight. When frac > 0, rem is replaced by
+// contiguous, conflict-free stretch. Returns the bucket b* with
+// weight(buckets > b*) < rem <= weight(buckets >= b*); *above = weight(buckets > b*),
+// *in = weight(b*). `lds` holds NT/64 elements, `pick` 3. Requires
+// 0 < rem <= total weight. When frac > 0, rem is replaced by
 // max(1, ceil(frac * total weight)) and *rem_used receives it, so a first pass needs no
 // separate reduction for the total. It ends without a barrier: every thread has read `lds`
 // before the second barrier and reads `pick` after it, so the caller must pass a block
