@@ -17,14 +17,15 @@ from tests import parity  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-# (config, p)
+# (config, p, width of the estimate's key codes)
 CASES = {
-    "cfg2-longchat-mha-32k": (2, 0.85),
-    "cfg3-llama-gqa-128k": (3, 0.9),
-    "cfg4-longchat-b32-ragged": (4, 0.85),
-    "cfg5-llama-gqa-b8-64k-p0.8": (5, 0.8),
-    "cfg5-llama-gqa-b8-64k-p0.9": (5, 0.9),
-    "cfg5-llama-gqa-b8-64k-p0.95": (5, 0.95),
+    "cfg2-longchat-mha-32k": (2, 0.85, 4),
+    "cfg3-llama-gqa-128k": (3, 0.9, 4),
+    "cfg3-llama-gqa-128k-2bit": (3, 0.9, 2),
+    "cfg4-longchat-b32-ragged": (4, 0.85, 4),
+    "cfg5-llama-gqa-b8-64k-p0.8": (5, 0.8, 4),
+    "cfg5-llama-gqa-b8-64k-p0.9": (5, 0.9, 4),
+    "cfg5-llama-gqa-b8-64k-p0.95": (5, 0.95, 4),
 }
 
 # oracle worker threads (at most the 16 host cores that go with one GPU), and units per
@@ -37,13 +38,13 @@ ORACLE_BATCH = 64
 @pytest.mark.parametrize("name", list(CASES))
 def test_full_size_step(name):
     from adaptive_top_sparse_amd import pipeline
-    cfg, p = CASES[name]
+    cfg, p, bits = CASES[name]
     print(f"\n[full size] {name}: generating", flush=True)
     w = workloads.make_workload(cfg)
     s = w.spec
     units = [(b, g) for b in range(s.B) for g in range(s.Hkv)]
     G = s.G
-    c = pipeline.upload(w)
+    c = pipeline.upload(w, key_bits=bits)
     c.build_caches()
     buf = pipeline.alloc_step(c)
     print(f"[full size] {name}: running the step", flush=True)
@@ -109,12 +110,13 @@ def test_full_size_step(name):
           f"{ORACLE_THREADS} threads", flush=True)
     sm = parity.sm_scale_for(s.d)
     for i0 in range(0, len(units), ORACLE_BATCH):
-        orc = parity.oracle_units(w, p, units[i0:i0 + ORACLE_BATCH], threads=ORACLE_THREADS)
+        orc = parity.oracle_units(w, p, units[i0:i0 + ORACLE_BATCH], key_bits=bits,
+                                  threads=ORACLE_THREADS)
         for (b, g), res in orc.items():
             n = int(w.seq_lens[b])
             codes = parity.logical_rows(codes_h, w.page_table[b], n, g)
             meta = parity.logical_rows(meta_h, w.page_table[b], n, g)
-            assert np.array_equal(parity.unpack_codes(codes), res["codes"]), (b, g)
+            assert np.array_equal(parity.unpack_codes(codes, bits), res["codes"]), (b, g)
             assert np.array_equal(meta[..., 0].astype(np.float64),
                                   res["scale"].astype(np.float64)), (b, g)
             assert np.array_equal(meta[..., 1].astype(np.float64),
