@@ -5,6 +5,8 @@ Quest and the weight estimate are shared with the group-wise step; top-p and dec
 query head. Each head's kept set and output are checked against the oracle, whose head-wise
 form is its top-p with G = 1 on that head's weights; with G = 1 the two modes coincide.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -95,14 +97,17 @@ def test_headwise_step_matches_oracle(name):
 
 
 @pytest.mark.timeout(600)
-def test_headwise_full_size_llama_gqa_128k():
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_headwise_full_size(cfg):
+    """The 128k GQA step (Quest base) and the B = 8, 64k full-attention step at full size,
+    head-wise: every query head's kept set and output against the oracle."""
     from adaptive_top_sparse_amd import pipeline
     p = 0.9
-    units = [(0, 3)]
-    print("\n[headwise] llama31-8b-gqa-n128k full size", flush=True)
-    w = workloads.make_workload(3)
+    w = workloads.make_workload(cfg)
     s = w.spec
     G = s.G
+    print(f"\n[headwise] {s.name} full size", flush=True)
+    units = [(b, g) for b in range(s.B) for g in range(s.Hkv)]
     c = pipeline.upload(w)
     c.build_caches()
     buf = pipeline.alloc_step(c, headwise=True)
@@ -111,26 +116,34 @@ def test_headwise_full_size_llama_gqa_128k():
     out = _host(buf)
     del c, buf
     torch.cuda.empty_cache()
-    n = int(w.seq_lens[0])
     # every head, at any size: kept ids are candidates, ascending, and carry p of the mass
-    for h in range(s.Hq):
-        g = h // G
-        k = out["kept"][0, h, :out["kept_count"][0, h]]
-        pages = out["sel_pages"][0, g, :out["sel_count"][0, g]]
-        toks = parity.slot_tokens(pages, w.budget * 16, n)
-        assert np.all(np.diff(k) > 0) and np.isin(k, toks[toks >= 0]).all()
-        W = out["weights"][0, h].astype(np.float64)
-        by_tok = dict(zip(toks[toks >= 0].tolist(), W[toks >= 0].tolist()))
-        total = sum(by_tok.values())
-        kept_w = np.array([by_tok[int(t)] for t in k])
-        assert kept_w.sum() >= p * total - 1e-6 * total
-        dropped = np.setdiff1d(toks[toks >= 0], k)
-        if dropped.size and kept_w.size:
-            assert max(by_tok[int(t)] for t in dropped) <= kept_w.min() * (1 + 1e-6)
-    orc = parity.oracle_units(w, p, units, headwise=True)
+    for b in range(s.B):
+        n = int(w.seq_lens[b])
+        for h in range(s.Hq):
+            g = h // G
+            k = out["kept"][b, h, :out["kept_count"][b, h]]
+            if out["sel_pages"] is not None:
+                pages = out["sel_pages"][b, g, :out["sel_count"][b, g]]
+                toks = parity.slot_tokens(pages, w.budget * 16, n)
+            else:
+                toks = parity.slot_tokens(None, out["weights"].shape[2], n)
+            assert np.all(np.diff(k) > 0) and np.isin(k, toks[toks >= 0]).all()
+            W = out["weights"][b, h].astype(np.float64)
+            by_tok = dict(zip(toks[toks >= 0].tolist(), W[toks >= 0].tolist()))
+            total = sum(by_tok.values())
+            kept_w = np.array([by_tok[int(t)] for t in k])
+            assert kept_w.sum() >= p * total - 1e-6 * total
+            dropped = np.setdiff1d(toks[toks >= 0], k)
+            if dropped.size and kept_w.size:
+                assert max(by_tok[int(t)] for t in dropped) <= kept_w.min() * (1 + 1e-6)
+    print(f"[headwise] {s.name}: oracle on all {len(units)} units", flush=True)
+    orc = parity.oracle_units(w, p, units, headwise=True,
+                              threads=max(1, min(16, os.cpu_count() or 1)))
     sm = parity.sm_scale_for(s.d)
     for (b, g), res in orc.items():
-        assert np.array_equal(out["sel_pages"][b, g, :out["sel_count"][b, g]], res["sel"])
+        n = int(w.seq_lens[b])
+        if out["sel_pages"] is not None:
+            assert np.array_equal(out["sel_pages"][b, g, :out["sel_count"][b, g]], res["sel"])
         parity.check_weights(out["weights"][b, g * G:(g + 1) * G], res["weights"], res["valid"])
         for j in range(G):
             h = g * G + j
@@ -139,3 +152,4 @@ def test_headwise_full_size_llama_gqa_128k():
             parity.check_kept(kept, rv, p, n)
             parity.check_out(out["out"][b, h:h + 1], w.q[b, h:h + 1], w.k[b][g], w.v[b][g],
                              kept, rv, sm)
+    print(f"[headwise] {s.name}: ok", flush=True)
