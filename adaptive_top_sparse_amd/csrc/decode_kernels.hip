@@ -215,7 +215,9 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
     return ((static_cast<long>(phys) * Hkv + kvh) * kPage + tok % kPage) * D;
   };
   // V rows (and in the dot2 form K rows) at the lane's channels; in the MFMA form the K
-  // operand of the lane's tile token. Dead rows read row 0 and are masked afterwards.
+  // operand of the lane's tile token. Dead rows read row 0 and are masked afterwards. A
+  // step reads each kept row once: non-temporal loads (measured 13.4 -> 12.9 us for decode
+  // + merge at the 128k GQA layer, 299 -> 285 us at the B = 8 64k full-attention step).
   auto load_kv = [&](const int (&phys)[NU], const int (&tok)[NU], bool (&live)[U],
                      u32x4 (&kx)[KX], u32x4 (&vv)[U]) {
 #pragma unroll
@@ -223,14 +225,16 @@ __attribute__((amdgpu_waves_per_eu(kSingle && G <= 4 ? 4 : 1))) void sparse_deco
       const long row = row_of(phys[u], tok[u]);
       live[u] = row >= 0;
       const long r = row >= 0 ? row : 0;
-      if constexpr (!kMfma) kx[u] = *reinterpret_cast<const u32x4*>(k_cache + r + c0);
-      vv[u] = *reinterpret_cast<const u32x4*>(v_cache + r + c0);
+      if constexpr (!kMfma)
+        kx[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + r + c0));
+      vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + r + c0));
     }
     if constexpr (kMfma) {
       const long row = row_of(phys[U], tok[U]);
       const uint16_t* kr = k_cache + (row >= 0 ? row : 0) + 8 * (lane / 16);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) kx[jj] = *reinterpret_cast<const u32x4*>(kr + 32 * jj);
+      for (int jj = 0; jj < 4; ++jj)
+        kx[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * jj));
     }
   };
 

@@ -105,13 +105,15 @@ __global__ __launch_bounds__(kScoreThreads) void quest_score_kernel(
   // this KV head's bounds, in logical page order; pages past the sequence load page p0
   // (so that no load sits behind a branch) and are not written
   const uint16_t* unit_mm = minmax + (static_cast<long>(b) * Hkv + g) * max_pages * 2 * D;
+  // The bounds are read once per step: non-temporal loads (measured 8.4 -> 7.7 us at the
+  // 128k GQA layer and 122 -> 116 us at the B = 32 ragged batch).
   u32x4 lo[ROUNDS], hi[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int p = p0 + r * PPI + threadIdx.x / LPP;
     const uint16_t* blk = unit_mm + static_cast<long>(p < P ? p : p0) * 2 * D + c0;
-    lo[r] = *reinterpret_cast<const u32x4*>(blk);
-    hi[r] = *reinterpret_cast<const u32x4*>(blk + D);
+    lo[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk));
+    hi[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(blk + D));
   }
   // A_c / B_c: sums of the group's negative / non-negative q_hc, formed once per block
   // (while the bounds are in flight) and read back per lane. Sums of at most 8 fp16 values
