@@ -171,8 +171,12 @@ int twilight_estimate_weights(const twl_layout_t* L, const void* q, const uint8_
  * group). W_j = mean over the group's G heads of weights[h, j] on the valid slots. tau is
  * the largest threshold whose kept mass sum_{W_j >= tau} W_j reaches p * sum_j W_j
  * (masses summed exactly in fixed point, in units of 2^-40 of the largest W's binade);
- * p == 1 prunes nothing: every valid slot is kept, whatever its W (0 included). The kept
- * slots are compacted into ascending logical token ids.
+ * p == 1 prunes nothing: every valid slot is kept, whatever its W (0 included). Below
+ * p = 1, a unit with no positive W keeps nothing, and W below 2^-126 (fp32 subnormals)
+ * carry no mass; a unit whose largest W is itself below 2^-126 has no fixed-point
+ * resolution left and may keep every valid slot (tau 0). Softmax weights never come near
+ * that case (their largest W is at least 1 / slots). The kept slots are compacted into
+ * ascending logical token ids.
  *   kept       : int32 [B, Hkv, cand_stride_pages * 16] (entries past kept_count untouched)
  *   kept_count : int32 [B, Hkv]
  *   tau        : fp32 [B, Hkv] or NULL; at p == 1 the smallest positive W (0 if none)
